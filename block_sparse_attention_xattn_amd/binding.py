@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libxattn.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU, passes their device pointers, sizes and
+strides, and enqueues on the current torch stream.  No arithmetic of the path
+happens in Python; if the library is missing the call raises.
+
+Layouts (batch = 1): q [q_len, Hq, d], k/v [kv_len, Hkv, d] (last dim
+contiguous); block masks / scores [Hq, q_len/128, n_key_blocks]; out
+[q_len, Hq, d]; lse [Hq, q_len].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxattn.so")
+
+XA_OK, XA_EINVAL, XA_EUNSUPPORTED, XA_EWORKSPACE, XA_EHIP = 0, 1, 2, 3, 4
+XA_F32, XA_BF16 = 0, 1
+STATUS_NAMES = {0: "XA_OK", 1: "XA_EINVAL", 2: "XA_EUNSUPPORTED", 3: "XA_EWORKSPACE", 4: "XA_EHIP"}
+
+_lib = None
+
+
+class XattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _declare(lib):
+    P, I64, I32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.xattn_last_error.restype = ctypes.c_char_p
+    lib.xattn_last_error.argtypes = []
+    lib.xattn_version.restype = ctypes.c_char_p
+    lib.xattn_version.argtypes = []
+    lib.xattn_estimate_workspace_size.restype = SZ
+    lib.xattn_estimate_workspace_size.argtypes = [I64, I64, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.xattn_estimate.restype = ctypes.c_int
+    lib.xattn_estimate.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
+                                   I64, I32, I32, F, P, P, P, SZ, P]
+    lib.bsa_prefill_workspace_size.restype = SZ
+    lib.bsa_prefill_workspace_size.argtypes = [I64, I64, I32, I32, I32, ctypes.c_int]
+    lib.bsa_prefill.restype = ctypes.c_int
+    lib.bsa_prefill.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
+                                I64, I64, P, I64, I64, I64, I32, I32, F, P, ctypes.c_int, P, P, SZ, P]
+    lib.attn_merge.restype = ctypes.c_int
+    lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
+    lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
+    lib.xattn_mask_to_cache_blocks.argtypes = [P, I32, I32, I64, I64, I64, I64, I64, I32, I32, P, P, P, P]
+    return lib
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_xattn_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(st: int):
+    if st != XA_OK:
+        raise XattnError(st, lib().xattn_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return XA_BF16
+    if t.dtype == torch.float32:
+        return XA_F32
+    raise XattnError(XA_EUNSUPPORTED, f"dtype {t.dtype} (bfloat16 or float32 only)")
+
+
+def _qkv_check(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise XattnError(XA_EINVAL, f"{name} must be a GPU tensor")
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise XattnError(XA_EINVAL, f"{name} must be [tokens, heads, head_dim] with a contiguous last dim")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A device byte buffer of at least nbytes (256-byte aligned by the caching allocator)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def xattn_estimate_workspace_size(q_len, k_len, num_q_heads, num_kv_heads, head_dim, stride, block=128,
+                                  dtype=XA_BF16) -> int:
+    return int(lib().xattn_estimate_workspace_size(q_len, k_len, num_q_heads, num_kv_heads, head_dim, stride,
+                                                   block, dtype))
+
+
+def bsa_prefill_workspace_size(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype=XA_BF16) -> int:
+    return int(lib().bsa_prefill_workspace_size(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype))
+
+
+def xattn_estimate(q, k, q_start_pos: int, stride: int = 8, threshold: float = 0.9, block: int = 128,
+                   block_scores=None, block_mask=None, ws=None, stream=None):
+    """Block scores and block mask of one query chunk (see xattn.h).  Returns (scores, mask)."""
+    _qkv_check(q, "q")
+    _qkv_check(k, "k")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype:
+        raise XattnError(XA_EINVAL, "q and k dtypes differ")
+    q_len, hq, d = q.shape
+    k_len, hkv, _ = k.shape
+    n_qb, nkb = q_len // block, k_len // block
+    if block_scores is None:
+        block_scores = torch.empty(hq, n_qb, nkb, dtype=torch.float32, device=q.device)
+    if block_mask is None:
+        block_mask = torch.empty(hq, n_qb, nkb, dtype=torch.uint8, device=q.device)
+    need = xattn_estimate_workspace_size(q_len, k_len, hq, hkv, d, stride, block, dt)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().xattn_estimate(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), dt,
+                                q_len, k_len, hq, hkv, d, q_start_pos, stride, block, float(threshold),
+                                _ptr(block_scores), _ptr(block_mask), _ptr(ws), ws.numel(), _stream(stream)))
+    return block_scores, block_mask
+
+
+def bsa_prefill(q, k, v, q_start_pos: int, kv_start: int, block_mask=None, mask_kb_offset: int = 0,
+                causal: bool = True, softmax_scale: float = 0.0, out_dtype=None, block: int = 128,
+                out=None, lse=None, ws=None, mask_head_stride=None, mask_row_stride=None, stream=None):
+    """Block-sparse attention with LSE (see xattn.h).  Returns (out, lse).
+
+    block_mask: uint8 [Hq, n_qb, n_cols] (or a broadcast view with zero strides), or None for dense.
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _qkv_check(t, nm)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise XattnError(XA_EINVAL, "q, k, v dtypes differ")
+    q_len, hq, d = q.shape
+    kv_len, hkv, _ = k.shape
+    if out_dtype is None:
+        out_dtype = q.dtype
+    odt = _dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty(q_len, hq, d, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(hq, q_len, dtype=torch.float32, device=q.device)
+    hs = rs = 0
+    if block_mask is not None:
+        if block_mask.dtype not in (torch.uint8, torch.bool) or block_mask.stride(-1) != 1:
+            raise XattnError(XA_EINVAL, "block_mask must be uint8/bool with a contiguous last dim")
+        hs = block_mask.stride(0) if mask_head_stride is None else mask_head_stride
+        rs = block_mask.stride(1) if mask_row_stride is None else mask_row_stride
+    need = bsa_prefill_workspace_size(q_len, kv_len, hq, hkv, d, dt)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().bsa_prefill(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+                             _ptr(v), v.stride(0), v.stride(1), dt, q_len, kv_len, hq, hkv, d,
+                             q_start_pos, kv_start, _ptr(block_mask), hs, rs, mask_kb_offset, block,
+                             1 if causal else 0, float(softmax_scale), _ptr(out), odt, _ptr(lse),
+                             _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
+    """LSE merge (see xattn.h); o_out / lse_out may alias the inputs.  Returns (o, lse)."""
+    q_len, heads, d = o_a.shape
+    for t in (o_a, o_b, lse_a, lse_b):
+        if not t.is_cuda or not t.is_contiguous():
+            raise XattnError(XA_EINVAL, "attn_merge needs contiguous GPU tensors")
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    _check(lib().attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out), _ptr(lse_out),
+                            _dtype_code(o_a), q_len, heads, d, _stream(stream)))
+    return o_out, lse_out
+
+
+def xattn_mask_to_cache_blocks(block_mask, kb_begin: int, n_cache_blocks: int, sub_blocks: int = 8,
+                               force_first_last: bool = True, keep_per_head=None, keep_any=None,
+                               keep_any_blocks=None, want=("per_head", "any", "any_blocks"), stream=None):
+    """Reduce a [H, n_qb, n_cols] block mask to cache blocks.  Returns (per_head, any, any_blocks)."""
+    H, n_qb, n_cols = block_mask.shape
+    dev = block_mask.device
+    if keep_per_head is None and "per_head" in want:
+        keep_per_head = torch.empty(H, n_qb, n_cache_blocks, dtype=torch.uint8, device=dev)
+    if keep_any is None and "any" in want:
+        keep_any = torch.empty(n_cache_blocks, dtype=torch.uint8, device=dev)
+    if keep_any_blocks is None and "any_blocks" in want:
+        keep_any_blocks = torch.empty(n_cache_blocks * sub_blocks, dtype=torch.uint8, device=dev)
+    _check(lib().xattn_mask_to_cache_blocks(_ptr(block_mask), H, n_qb, n_cols, block_mask.stride(0),
+                                            block_mask.stride(1), kb_begin, n_cache_blocks, sub_blocks,
+                                            1 if force_first_last else 0, _ptr(keep_per_head), _ptr(keep_any),
+                                            _ptr(keep_any_blocks), _stream(stream)))
+    return keep_per_head, keep_any, keep_any_blocks

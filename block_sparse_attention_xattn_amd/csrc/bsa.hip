@@ -1,0 +1,485 @@
+// Block-sparse flash attention with LSE (part 2 of the path).
+//
+// XAttention algorithm guide, "BSA (Block Sparse Attention)": exact softmax
+// attention restricted to the 128x128 (query block, key block) tiles that the
+// block mask keeps, with token causality; XAttentionBSAPolicy
+// .compute_chunked_prefill: the history segment is attended without the
+// causal rule, the chunk's own keys with it, and each part returns (out, lse).
+//
+// Kernel design (gfx950):
+//   * one workgroup = one (query head, 128-row query block); 8 waves.  Wave w
+//     owns query rows 32*(w%4) .. +32 and key half 64*(w/4) .. +64 of every
+//     kept key block (split over keys inside the workgroup; the two halves are
+//     merged once at the end through LDS);
+//   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     a lane then owns one query row and 16 keys, so the row max / row sum are
+//     mostly in-lane (one cross-half exchange per block for the max);
+//   * the fp32 accumulator of S^T, exponentiated and rounded to bf16, is
+//     directly the B operand of the O^T += V^T P^T MFMA; V is stored transposed
+//     in the workspace with the matching key order inside each 16-key group,
+//     so both operands come from LDS with 16-byte reads;
+//   * K and V^T tiles of the next kept block are fetched into registers while
+//     the current one is being multiplied (two LDS buffers);
+//   * the walk over key blocks touches only kept blocks, in ascending order,
+//     from a list built in LDS from the mask row.
+// XA_F32 inputs use bf16 hi/lo planes and three MFMAs per product.
+#include "launchers.h"
+
+namespace xa {
+
+
+constexpr int kBlk = 128;
+constexpr int kThreads = 512;
+constexpr int kListMax = 1024;
+
+// Work order: clusters of (kv head, query block), heaviest query blocks first;
+// the `group` query heads of a cluster get consecutive dispatch slots on the
+// same XCD (ids b, b+8, b+16, ...), so they read the same K/V tiles through
+// one L2.
+__device__ __forceinline__ void bsa_decode(int bid, int group, int hkv, int n_qb, int& h, int& qb) {
+  const int clusters = hkv * n_qb;
+  const int full_rounds = clusters / 8;
+  const int full_ids = full_rounds * 8 * group;
+  int c, j;
+  if (bid < full_ids) {
+    const int x = bid & 7;
+    const int t = bid >> 3;
+    j = t % group;
+    c = (t / group) * 8 + x;
+  } else {
+    const int rem = bid - full_ids;
+    c = full_rounds * 8 + rem / group;
+    j = rem % group;
+  }
+  qb = n_qb - 1 - c / hkv;
+  h = (c % hkv) * group + j;
+}
+
+template <int D, bool SPLIT, typename OutT>
+__global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
+  constexpr int PLANES = SPLIT ? 2 : 1;
+  constexpr int NBUF = SPLIT ? 1 : 2;
+  constexpr int KP = D + 8;       // K tile pitch (elements): rows 16 B apart mod 128 B
+  constexpr int VP = kBlk + 8;    // V^T tile pitch
+  constexpr int KT = kBlk * KP;   // K tile elements per plane
+  constexpr int VT = D * VP;      // V^T tile elements per plane
+  constexpr int STAGE = PLANES * (KT + VT);
+  constexpr int KCH = D / 32;     // 16-byte chunks per thread per K tile (and per V^T tile)
+  constexpr int NKK = D / 16;     // MFMA k-steps over head_dim
+  constexpr int NMD = D / 32;     // 32-row tiles of O^T
+
+  __shared__ __attribute__((aligned(16))) bf16 smem[NBUF * STAGE];
+  __shared__ int s_list[kListMax];
+  __shared__ int s_cnt;
+
+  const int tid = threadIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int wq = wave & 3;
+  const int wk = wave >> 2;
+
+  int h, qb;
+  bsa_decode(blockIdx.x, P.group, P.hkv, P.n_qb, h, qb);
+  const int kvh = h / P.group;
+
+  const int64_t row = (int64_t)qb * kBlk + wq * 32 + n;  // this lane's query row
+  const int64_t q_glob = P.q_start + row;
+  const int64_t wave_q_lo = P.q_start + (int64_t)qb * kBlk + wq * 32;
+  const int64_t wave_q_hi = wave_q_lo + 31;
+
+  // ---- query fragments (B operand of S^T = K Q^T), kept in registers
+  bf16x8 qf[PLANES][NKK];
+  {
+    const int64_t off = row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[0][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q_hi + off + kk * 16));
+      if constexpr (SPLIT) qf[1][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q_lo + off + kk * 16));
+    }
+  }
+
+  f32x16 o[NMD];
+#pragma unroll
+  for (int i = 0; i < NMD; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // ---- key-block range of this call
+  const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
+  const int64_t gb0 = P.kv_start / kBlk;
+  int64_t jb_end = nkb;
+  if (P.causal) {
+    const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
+    jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
+  }
+  const uint8_t* mrow = P.mask ? P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
+
+  const bf16* kpl[2] = {P.k_hi, P.k_lo};
+  const bf16* vpl[2] = {P.vt_hi, P.vt_lo};
+  const int64_t kbase = (int64_t)kvh * P.k_head;
+  const int64_t vbase = (int64_t)kvh * P.vt_head;
+
+  u32x4 rk[PLANES][KCH], rv[PLANES][KCH];
+
+  auto load_regs = [&](int jb) {
+    const int64_t j0 = (int64_t)jb * kBlk;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / (D / 8);
+      const int c8 = c % (D / 8);
+      const bool ok = j0 + r < P.kv_len;
+      const int64_t off = kbase + (j0 + r) * P.k_tok + c8 * 8;
+#pragma unroll
+      for (int pl = 0; pl < PLANES; ++pl)
+        rk[pl][i] = ok ? *reinterpret_cast<const u32x4*>(kpl[pl] + off) : u32x4{0, 0, 0, 0};
+      const int d = c / (kBlk / 8);
+      const int k8 = c % (kBlk / 8);
+      const int64_t voff = vbase + (int64_t)d * P.vt_pitch + j0 + k8 * 8;
+#pragma unroll
+      for (int pl = 0; pl < PLANES; ++pl) rv[pl][i] = *reinterpret_cast<const u32x4*>(vpl[pl] + voff);
+    }
+  };
+  auto store_lds = [&](int buf) {
+    bf16* st = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / (D / 8);
+      const int c8 = c % (D / 8);
+      const int d = c / (kBlk / 8);
+      const int k8 = c % (kBlk / 8);
+#pragma unroll
+      for (int pl = 0; pl < PLANES; ++pl) {
+        *reinterpret_cast<u32x4*>(st + pl * (KT + VT) + r * KP + c8 * 8) = rk[pl][i];
+        *reinterpret_cast<u32x4*>(st + pl * (KT + VT) + KT + d * VP + k8 * 8) = rv[pl][i];
+      }
+    }
+  };
+
+  auto compute = [&](int buf, int jb) {
+    const int64_t key0 = (int64_t)jb * kBlk + wk * 64;      // local index of this wave's first key
+    const int64_t gkey0 = P.kv_start + key0;
+    if (P.causal && gkey0 > wave_q_hi) return;              // this key half is entirely in the future
+    if (key0 >= P.kv_len) return;                           // past the tail
+    const bool need_mask = (key0 + 64 > P.kv_len) || (P.causal && gkey0 + 63 > wave_q_lo);
+    const bf16* st = smem + buf * STAGE;
+
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int key = wk * 64 + mt * 32 + n;
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(st + key * KP + kk * 16 + 8 * hh));
+        s[mt] = mfma32(a, qf[0][kk], s[mt]);
+        if constexpr (SPLIT) {
+          const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4*>(st + (KT + VT) + key * KP + kk * 16 + 8 * hh));
+          s[mt] = mfma32(a, qf[1][kk], s[mt]);
+          s[mt] = mfma32(alo, qf[0][kk], s[mt]);
+        }
+      }
+    }
+
+    // scale into log2 units, mask, running max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = s[mt][i] * P.scale_log2;
+        if (need_mask) {
+          const int64_t kl = key0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+          const bool ok = kl < P.kv_len && (!P.causal || P.kv_start + kl <= q_glob);
+          x = ok ? x : -INFINITY;
+        }
+        s[mt][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - ref);
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(s[mt][i] - ref);
+        s[mt][i] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) o[md] *= alpha;
+
+    // P^T fragments straight from the accumulator registers
+    bf16x8 pf[PLANES][4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = s[k2 >> 1][8 * (k2 & 1) + j];
+        if constexpr (SPLIT) {
+          bf16 hi, lo;
+          split_bf16(p, hi, lo);
+          pf[0][k2][j] = hi;
+          pf[1][k2][j] = lo;
+        } else {
+          pf[0][k2][j] = (bf16)p;
+        }
+      }
+    }
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int d = md * 32 + n;
+        const int col = wk * 64 + k2 * 16 + 8 * hh;
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(st + KT + d * VP + col));
+        o[md] = mfma32(a, pf[0][k2], o[md]);
+        if constexpr (SPLIT) {
+          const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4*>(st + (KT + VT) + KT + d * VP + col));
+          o[md] = mfma32(a, pf[1][k2], o[md]);
+          o[md] = mfma32(alo, pf[0][k2], o[md]);
+        }
+      }
+    }
+  };
+
+  // ---- walk the kept blocks, kListMax at a time
+  for (int64_t seg = 0; seg < jb_end; seg += kListMax) {
+    const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
+    if (wave == 0) {
+      int cnt = 0;
+      for (int64_t base = seg; base < seg_end; base += 64) {
+        const int64_t jb = base + lane;
+        const bool keep = jb < seg_end && (mrow == nullptr || mrow[jb] != 0);
+        const uint64_t bal = __ballot(keep);
+        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1));
+        if (keep) s_list[pos] = (int)jb;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) s_cnt = cnt;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    if (cnt > 0) {
+      load_regs(s_list[0]);
+      store_lds(0);
+      __syncthreads();
+      for (int it = 0; it < cnt; ++it) {
+        const int jb = s_list[it];
+        if constexpr (NBUF == 2) {
+          const int buf = it & 1;
+          if (it + 1 < cnt) load_regs(s_list[it + 1]);
+          compute(buf, jb);
+          if (it + 1 < cnt) store_lds(buf ^ 1);
+          __syncthreads();
+        } else {
+          compute(0, jb);
+          __syncthreads();
+          if (it + 1 < cnt) {
+            load_regs(s_list[it + 1]);
+            store_lds(0);
+          }
+          __syncthreads();
+        }
+      }
+    }
+    __syncthreads();  // s_list / s_cnt are rewritten by the next segment
+  }
+
+  // ---- merge the two key halves of each query row, normalise, write
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  float* xch = reinterpret_cast<float*>(smem);  // [4][NMD*16 + 2][64]
+  constexpr int XV = NMD * 16 + 2;
+  if (wk == 1) {
+    float* dst = xch + wq * XV * 64;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[(md * 16 + i) * 64 + lane] = o[md][i];
+    dst[(NMD * 16) * 64 + lane] = m_run;
+    dst[(NMD * 16 + 1) * 64 + lane] = l_row;
+  }
+  __syncthreads();
+  if (wk == 0) {
+    const float* src = xch + wq * XV * 64;
+    const float m1 = src[(NMD * 16) * 64 + lane];
+    const float l1 = src[(NMD * 16 + 1) * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    float a0 = 0.f, a1 = 0.f, lse_v = -INFINITY, inv = 0.f;
+    if (m != -INFINITY) {
+      a0 = fast_exp2(m_run - m);
+      a1 = fast_exp2(m1 - m);
+      const float l = l_row * a0 + l1 * a1;
+      inv = 1.f / l;
+      lse_v = (m + log2f(l)) * kLn2;
+    }
+    OutT* out = reinterpret_cast<OutT*>(P.out);
+    const int64_t obase = row * ((int64_t)P.hq * D) + (int64_t)h * D;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = g4 * 4 + e;
+          v[e] = (o[md][i] * a0 + src[(md * 16 + i) * 64 + lane] * a1) * inv;
+        }
+        if constexpr (sizeof(OutT) == 2) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = (bf16)v[e];
+          *reinterpret_cast<u32x2*>(out + obase + d0) = __builtin_bit_cast(u32x2, pk);
+        } else {
+          *reinterpret_cast<f32x4*>(out + obase + d0) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+    if (hh == 0) P.lse[(int64_t)h * P.q_len + row] = lse_v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Workspace preparation
+// ---------------------------------------------------------------------------
+
+// V [kv_len][hkv][D] (token-major, strided) -> Vt[hkv][D][pitch] in bf16
+// (hi and optionally lo planes), keys permuted by kSigma inside each group of
+// 16, zero beyond kv_len.  64x64 tiles through LDS for coalesced reads/writes.
+template <typename T, bool SPLIT>
+__global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, int64_t v_tok, int64_t v_head,
+                                                 int64_t kv_len, int D, bf16* vt_hi, bf16* vt_lo,
+                                                 int64_t pitch) {
+  __shared__ float tile[64][65];
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const int d0 = blockIdx.y * 64;
+  const int kvh = blockIdx.z;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < 64 * 8; c += 256) {
+    const int kr = c / 8, dc = (c % 8) * 8;
+    const int64_t key = k0 + kr;
+    float vals[8];
+    if (key < kv_len) {
+      const T* src = v + key * v_tok + (int64_t)kvh * v_head + d0 + dc;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 x = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vals[j] = (float)x[j];
+      } else {
+        const f32x4 a = reinterpret_cast<const f32x4*>(src)[0];
+        const f32x4 b = reinterpret_cast<const f32x4*>(src)[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vals[j] = a[j];
+          vals[4 + j] = b[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vals[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[dc + j][kr] = vals[j];
+  }
+  __syncthreads();
+  for (int c = tid; c < 64 * 8; c += 256) {
+    const int dr = c / 8, pc = (c % 8) * 8;
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pos = pc + j;
+      const int key = (pos & ~15) | kSigma(pos & 15);
+      const float x = tile[dr][key];
+      if constexpr (SPLIT) {
+        bf16 a, b;
+        split_bf16(x, a, b);
+        hi[j] = a;
+        lo[j] = b;
+      } else {
+        hi[j] = (bf16)x;
+      }
+    }
+    const int64_t off = ((int64_t)kvh * D + d0 + dr) * pitch + k0 + pc;
+    *reinterpret_cast<u32x4*>(vt_hi + off) = as_u32x4(hi);
+    if constexpr (SPLIT) *reinterpret_cast<u32x4*>(vt_lo + off) = as_u32x4(lo);
+  }
+}
+
+// fp32 [L][H][D] (strided) -> dense bf16 hi and lo planes [L][H][D].
+__global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x, int64_t tok, int64_t head,
+                                                    int64_t L, int H, int D, bf16* hi, bf16* lo) {
+  const int64_t chunks = L * H * (D / 8);
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = c / (H * (D / 8));
+    const int hd = (int)(c % (H * (D / 8)));
+    const int hh = hd / (D / 8);
+    const int d = (hd % (D / 8)) * 8;
+    const float* src = x + t * tok + (int64_t)hh * head + d;
+    const f32x4 a = reinterpret_cast<const f32x4*>(src)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(src)[1];
+    bf16x8 h8, l8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = j < 4 ? a[j] : b[j - 4];
+      bf16 p, q;
+      split_bf16(v, p, q);
+      h8[j] = p;
+      l8[j] = q;
+    }
+    const int64_t off = c * 8;
+    *reinterpret_cast<u32x4*>(hi + off) = as_u32x4(h8);
+    *reinterpret_cast<u32x4*>(lo + off) = as_u32x4(l8);
+  }
+}
+
+// Explicit instantiation helpers used by the ABI layer.
+template <int D, bool SPLIT, typename OutT>
+hipError_t launch_bsa(const BsaParams& p, hipStream_t s) {
+  const int grid = p.hq * p.n_qb;
+  hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template hipError_t launch_bsa<64, false, bf16>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<64, false, float>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<64, true, bf16>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<64, true, float>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<128, false, bf16>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<128, false, float>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<128, true, bf16>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<128, true, float>(const BsaParams&, hipStream_t);
+
+hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t kv_len, int hkv,
+                     int D, bf16* vt_hi, bf16* vt_lo, int64_t pitch, hipStream_t s) {
+  dim3 grid((unsigned)(pitch / 64), (unsigned)(D / 64), (unsigned)hkv);
+  if (dt == XA_BF16)
+    hipLaunchKernelGGL((vt_kernel<bf16, false>), grid, dim3(256), 0, s, (const bf16*)v, v_tok, v_head, kv_len,
+                       D, vt_hi, vt_lo, pitch);
+  else
+    hipLaunchKernelGGL((vt_kernel<float, true>), grid, dim3(256), 0, s, (const float*)v, v_tok, v_head, kv_len,
+                       D, vt_hi, vt_lo, pitch);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,
+                        hipStream_t s) {
+  const int64_t chunks = L * H * (D / 8);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, tok, head, L, H, D, hi, lo);
+  return hipGetLastError();
+}
+
+}  // namespace xa

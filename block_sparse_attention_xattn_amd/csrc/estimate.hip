@@ -1,0 +1,325 @@
+// XAttention importance estimate and block selection (part 1 of the path).
+//
+// XAttention algorithm guide (nano-vllm docs): "Stride Reshape 详解 / Inverse
+// 模式" (row r of the reshaped Q is Q[r*S+S-1-t] concatenated over t, column c
+// of the reshaped K is K[c*S+t] over t), "Triton Kernels 详解"
+// (flat_group_gemm_fuse_reshape computes the product without materialising the
+// reshaped tensors; softmax_fuse_block_sum normalises each row and sums
+// block_size/stride x block_size/stride tiles), "块选择算法" (cumulative
+// threshold with sink and diagonal kept).  Chunk placement and the
+// 1/(S*sqrt(d)) scale follow XAttentionBSAPolicy.select_blocks.
+//
+// Two kernels instead of the pages' recompute-twice passes:
+//   est_gemm_kernel   -- reshaped Q K^T on MFMA (the reshape is pure
+//                        addressing: stage t of the contraction stages the
+//                        query tokens r*S+S-1-t and key tokens c*S+t), then
+//                        per (row, key block) the log-sum-exp of the visible
+//                        scores, written once ([Hq][nKB][R], fp32, log2 units);
+//   est_select_kernel -- per (head, query block): row normaliser = log-sum-exp
+//                        over key blocks, block score = sum over the block's
+//                        rows of exp2(lse_part - row lse), then the threshold
+//                        selection (bitonic sort in LDS + prefix sums).
+// The block scores therefore need one GEMM pass, not two.
+#include "launchers.h"
+
+namespace xa {
+
+
+constexpr int kEThreads = 256;
+
+template <int D, bool SPLIT, int HALF>
+__global__ __launch_bounds__(kEThreads) void est_gemm_kernel(EstParams P) {
+  constexpr int TP = D + 8;          // LDS tile pitch (elements)
+  constexpr int TILE = 128 * TP;
+  constexpr int NKK = D / 16;
+  constexpr int CH = 128 * (D / 8) / kEThreads;  // 16-B chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * TILE];
+  bf16* qs = smem;
+  bf16* ks = smem + TILE;
+
+  const int tid = threadIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int wr = wave & 1;   // 64-row half of the tile
+  const int wc = wave >> 1;  // 64-column half of the tile
+
+  // work order: (kv head, column tile, row tile, head-in-group), last fastest
+  const int total = P.hkv * P.n_ct * P.n_rt * P.group;
+  int w = xcd_remap(blockIdx.x, total);
+  const int j = w % P.group;
+  w /= P.group;
+  const int rt = w % P.n_rt;
+  w /= P.n_rt;
+  const int ct = w % P.n_ct;
+  const int kvh = w / P.n_ct;
+  const int h = kvh * P.group + j;
+
+  const int64_t cdiag = P.q_start / P.S;  // column c visible to row r iff c <= cdiag + r
+  const int r_hi = min(P.R - 1, rt * 128 + 127);
+  if ((int64_t)ct * 128 > cdiag + r_hi) return;  // tile entirely right of the causal limit
+
+  const int w_r0 = rt * 128 + wr * 64;
+  const int w_c0 = ct * 128 + wc * 64;
+  const bool wave_live = w_r0 < P.R && w_c0 < P.N && (int64_t)w_c0 <= cdiag + min(P.R - 1, w_r0 + 63);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+
+  const int combos = SPLIT ? 3 : 1;
+  for (int t = 0; t < P.S; ++t) {
+    for (int cb = 0; cb < combos; ++cb) {
+      const bf16* qsrc = (cb == 2) ? P.q_lo : P.q_hi;
+      const bf16* ksrc = (cb == 1) ? P.k_lo : P.k_hi;
+      u32x4 rq[CH], rk[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + kEThreads * i;
+        const int r = c / (D / 8);
+        const int c8 = c % (D / 8);
+        const int64_t qr = (int64_t)rt * 128 + r;
+        const int64_t qtok = qr * P.S + (P.S - 1 - t);
+        rq[i] = qr < P.R ? *reinterpret_cast<const u32x4*>(qsrc + qtok * P.q_tok + (int64_t)h * P.q_head + c8 * 8)
+                         : u32x4{0, 0, 0, 0};
+        const int64_t kc = (int64_t)ct * 128 + r;
+        const int64_t ktok = kc * P.S + t;
+        rk[i] = kc < P.N ? *reinterpret_cast<const u32x4*>(ksrc + ktok * P.k_tok + (int64_t)kvh * P.k_head + c8 * 8)
+                         : u32x4{0, 0, 0, 0};
+      }
+      __syncthreads();  // previous stage's reads are done
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + kEThreads * i;
+        const int r = c / (D / 8);
+        const int c8 = c % (D / 8);
+        *reinterpret_cast<u32x4*>(qs + r * TP + c8 * 8) = rq[i];
+        *reinterpret_cast<u32x4*>(ks + r * TP + c8 * 8) = rk[i];
+      }
+      __syncthreads();
+      if (wave_live) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          bf16x8 af[2], bfr[2];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            af[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (wc * 64 + mt * 32 + n) * TP + kk * 16 + 8 * hh));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            bfr[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + (wr * 64 + nt * 32 + n) * TP + kk * 16 + 8 * hh));
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(af[mt], bfr[nt], acc[mt][nt]);
+        }
+      }
+    }
+  }
+  if (!wave_live) return;
+
+  // Epilogue: per (row, key block) log2-sum-exp2 of the visible scores.
+  // Lane values v = 16*mt + i sit at column 32*mt + 8*(i/4) + 4*hh + i%4 of the
+  // wave's 64 columns, so a key block (b columns) is a run of b/2 values per
+  // lane, the other half held by lane ^ 32.
+  static_assert(HALF == 4 || HALF == 8 || HALF == 16 || HALF == 32, "key block = 2*HALF reshaped columns");
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = w_r0 + nt * 32 + n;
+    float x[32];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+        const bool ok = c < P.N && c <= cdiag + r;
+        x[mt * 16 + i] = ok ? acc[mt][nt][i] * P.scale_log2 : -INFINITY;
+      }
+#pragma unroll
+    for (int g0 = 0; g0 < 32; g0 += HALF) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = g0; v < g0 + HALF; ++v) mx = fmaxf(mx, x[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float s = 0.f;
+      const float ref = mx == -INFINITY ? 0.f : mx;
+#pragma unroll
+      for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(x[v] - ref);
+      s += __shfl_xor(s, 32);
+      const int kb = w_c0 / (2 * HALF) + g0 / HALF;
+      if (hh == 0 && r < P.R && kb < P.nkb)
+        P.lse_part[((int64_t)h * P.nkb + kb) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block sums + cumulative-threshold selection, one workgroup per
+// (head, query block).
+// ---------------------------------------------------------------------------
+
+constexpr int kSortMax = 8192;
+
+__global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
+  __shared__ unsigned long long keys[kSortMax];
+  __shared__ uint8_t mrow[kSortMax];
+  __shared__ float row_lse[64];
+  __shared__ float red_m[256];
+  __shared__ float red_s[256];
+  __shared__ double part[256];
+  __shared__ double s_total;
+  __shared__ float s_a0, s_ad;
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x / P.n_qb;
+  const int qb = blockIdx.x % P.n_qb;
+  const int b = P.b;
+  const int64_t diag = P.cur + qb;  // always-kept diagonal block
+  const int nvis = (int)diag + 1;   // key blocks 0..diag
+  const float* base = P.lse_part + (int64_t)h * P.nkb * P.R + (int64_t)qb * b;
+
+  // pass 1: per-row normaliser over key blocks (log2 units)
+  {
+    const int r = tid % b;
+    const int stripe = tid / b;
+    const int nstripe = 256 / b;
+    float m = -INFINITY, s = 0.f;
+    for (int kb = stripe; kb < nvis; kb += nstripe) {
+      const float v = base[(int64_t)kb * P.R + r];
+      if (v == -INFINITY) continue;
+      if (v > m) {
+        s = s * fast_exp2(m - v) + 1.f;
+        m = v;
+      } else {
+        s += fast_exp2(v - m);
+      }
+    }
+    red_m[tid] = m;
+    red_s[tid] = s;
+    __syncthreads();
+    if (tid < b) {
+      float M = -INFINITY;
+      for (int k = 0; k < nstripe; ++k) M = fmaxf(M, red_m[k * b + tid]);
+      float S = 0.f;
+      for (int k = 0; k < nstripe; ++k) {
+        const float mk = red_m[k * b + tid];
+        if (mk != -INFINITY) S += red_s[k * b + tid] * fast_exp2(mk - M);
+      }
+      row_lse[tid] = M + log2f(S);
+    }
+    __syncthreads();
+  }
+
+  // pass 2: block scores, sort keys, row total
+  const bool all = P.threshold >= 1.0f;
+  int npow = 1;
+  while (npow < nvis) npow <<= 1;
+  double tsum = 0.0;
+  for (int kb = tid; kb < P.nkb; kb += 256) {
+    float a = 0.f;
+    if (kb < nvis) {
+      const float* col = base + (int64_t)kb * P.R;
+      for (int r = 0; r < b; ++r) {
+        const float v = col[r];
+        if (v != -INFINITY) a += fast_exp2(v - row_lse[r]);
+      }
+      tsum += a;
+    }
+    P.scores[((int64_t)h * P.n_qb + qb) * P.nkb + kb] = a;
+    const bool forced = kb == 0 || kb == diag;
+    if (kb < kSortMax) mrow[kb] = (kb < nvis && (all || forced)) ? 1 : 0;
+    if (kb < npow && kb < kSortMax) {
+      const unsigned bits = __float_as_uint(a);
+      keys[kb] = (kb < nvis && !forced) ? (((unsigned long long)(0xffffffffu - bits) << 32) | (unsigned)kb)
+                                         : ~0ull;
+    }
+    if (kb == 0) s_a0 = a;
+    if (kb == diag) s_ad = a;
+  }
+  for (int kb = P.nkb + tid; kb < npow; kb += 256) keys[kb] = ~0ull;
+  part[tid] = tsum;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int k = 0; k < 256; ++k) t += part[k];
+    s_total = t;
+  }
+  __syncthreads();
+
+  const int n_other = nvis - 2 > 0 ? nvis - 2 : 0;  // sortable blocks (0 and diag excluded)
+  if (!all && n_other > 0) {
+    // bitonic sort, ascending key = descending score, then ascending index
+    for (int k = 2; k <= npow; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < npow; i += 256) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const unsigned long long x = keys[i], y = keys[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              keys[i] = y;
+              keys[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // prefix mass over the sorted order: contiguous segments per thread
+    const int seg = (n_other + 255) / 256;
+    const int p0 = tid * seg;
+    const int p1 = min(n_other, p0 + seg);
+    double loc = 0.0;
+    for (int p = p0; p < p1; ++p) loc += (double)__uint_as_float(0xffffffffu - (unsigned)(keys[p] >> 32));
+    part[tid] = loc;
+    __syncthreads();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int k = 0; k < 256; ++k) {
+        const double v = part[k];
+        part[k] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    const double forced_mass = (double)s_a0 + (diag > 0 ? (double)s_ad : 0.0);
+    const double need = (double)P.threshold * s_total;
+    double run = forced_mass + part[tid];
+    for (int p = p0; p < p1; ++p) {
+      const unsigned long long key = keys[p];
+      if (run < need) mrow[(unsigned)(key & 0xffffffffu)] = 1;
+      run += (double)__uint_as_float(0xffffffffu - (unsigned)(key >> 32));
+    }
+    __syncthreads();
+  } else {
+    __syncthreads();
+  }
+  uint8_t* out = P.mask + ((int64_t)h * P.n_qb + qb) * P.nkb;
+  for (int kb = tid; kb < P.nkb; kb += 256) out[kb] = mrow[kb];
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_est_gemm(const EstParams& p, hipStream_t s) {
+  const int grid = p.hkv * p.n_ct * p.n_rt * p.group;
+  switch (p.b) {
+    case 8: hipLaunchKernelGGL((est_gemm_kernel<D, SPLIT, 4>), dim3(grid), dim3(kEThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((est_gemm_kernel<D, SPLIT, 8>), dim3(grid), dim3(kEThreads), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((est_gemm_kernel<D, SPLIT, 16>), dim3(grid), dim3(kEThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((est_gemm_kernel<D, SPLIT, 32>), dim3(grid), dim3(kEThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_est_gemm<64, false>(const EstParams&, hipStream_t);
+template hipError_t launch_est_gemm<64, true>(const EstParams&, hipStream_t);
+template hipError_t launch_est_gemm<128, false>(const EstParams&, hipStream_t);
+template hipError_t launch_est_gemm<128, true>(const EstParams&, hipStream_t);
+
+hipError_t launch_est_select(const SelParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(est_select_kernel, dim3(p.hq * p.n_qb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace xa

@@ -1,0 +1,64 @@
+// Kernel parameter blocks and launchers shared by the kernels and the C ABI.
+#pragma once
+
+#include "common.h"
+
+namespace xa {
+
+// Block-sparse attention (bsa.hip).
+struct BsaParams {
+  const bf16* q_hi;
+  const bf16* q_lo;
+  int64_t q_tok, q_head;
+  const bf16* k_hi;
+  const bf16* k_lo;
+  int64_t k_tok, k_head;
+  const bf16* vt_hi;
+  const bf16* vt_lo;
+  int64_t vt_head, vt_pitch;  // Vt[hkv][d][vt_pitch], key order permuted per 16-group
+  int64_t q_len, kv_len;
+  int hq, hkv, group, n_qb;
+  int64_t q_start, kv_start;
+  const uint8_t* mask;
+  int64_t mask_hs, mask_rs, mask_off;
+  int causal;
+  float scale_log2;
+  void* out;
+  float* lse;
+};
+
+// Reshaped GEMM + per-(row, key block) log-sum-exp (estimate.hip).
+struct EstParams {
+  const bf16* q_hi;
+  const bf16* q_lo;
+  int64_t q_tok, q_head;
+  const bf16* k_hi;
+  const bf16* k_lo;
+  int64_t k_tok, k_head;
+  int64_t q_len, k_len, q_start;
+  int hq, hkv, group, S, b, R, N, nkb, n_rt, n_ct;
+  float scale_log2;
+  float* lse_part;  // [hq][nkb][R], log2 units
+};
+
+// Block sums + threshold selection (estimate.hip).
+struct SelParams {
+  const float* lse_part;
+  int R, nkb, b, hq, n_qb;
+  int64_t cur;  // key blocks before the chunk (q_start / 128)
+  float threshold;
+  float* scores;  // [hq][n_qb][nkb]
+  uint8_t* mask;  // [hq][n_qb][nkb]
+};
+
+template <int D, bool SPLIT, typename OutT>
+hipError_t launch_bsa(const BsaParams& p, hipStream_t s);
+hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t kv_len, int hkv, int D,
+                     bf16* vt_hi, bf16* vt_lo, int64_t pitch, hipStream_t s);
+hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,
+                        hipStream_t s);
+template <int D, bool SPLIT>
+hipError_t launch_est_gemm(const EstParams& p, hipStream_t s);
+hipError_t launch_est_select(const SelParams& p, hipStream_t s);
+
+}  // namespace xa

@@ -1,0 +1,70 @@
+// 128-token block mask -> cache blocks (the reducer feeding block loads).
+//
+// Task plan page, "select_blocks 设计" step 3: a 1024-token cache block is
+// kept if any of its eight 128-token blocks is selected.
+// XAttentionBSAPolicy.select_blocks step 6: union over heads and query blocks,
+// then the first and last history block are always included.
+#include "common.h"
+
+namespace xa {
+
+// One workgroup per cache block.  Threads stride over the (head, query block)
+// rows; each reads its row's sub_blocks mask bytes, writes the per-head byte
+// and votes into the union.
+__global__ __launch_bounds__(256) void cache_block_kernel(
+    const uint8_t* __restrict__ mask, int heads, int n_qb, int64_t n_cols, int64_t hs, int64_t rs,
+    int64_t kb_begin, int64_t n_cb, int sub, int force_first_last, uint8_t* keep_per_head,
+    uint8_t* keep_any, uint8_t* keep_any_blocks) {
+  const int64_t cb = blockIdx.x;
+  const int64_t c0 = kb_begin + cb * sub;
+  int64_t c1 = c0 + sub;
+  if (c1 > n_cols) c1 = n_cols;
+  const int rows = heads * n_qb;
+  int any = 0;
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+    const int h = r / n_qb, qb = r % n_qb;
+    const uint8_t* row = mask + h * hs + qb * rs;
+    int hit = 0;
+    for (int64_t c = c0; c < c1; ++c) hit |= row[c];
+    hit = hit ? 1 : 0;
+    if (keep_per_head) keep_per_head[((int64_t)h * n_qb + qb) * n_cb + cb] = (uint8_t)hit;
+    any |= hit;
+  }
+  any = __syncthreads_or(any);
+  if (force_first_last && (cb == 0 || cb == n_cb - 1)) any = 1;
+  if (threadIdx.x == 0 && keep_any) keep_any[cb] = (uint8_t)any;
+  if (keep_any_blocks)
+    for (int s = threadIdx.x; s < sub; s += blockDim.x) keep_any_blocks[cb * sub + s] = (uint8_t)any;
+}
+
+}  // namespace xa
+
+using namespace xa;
+
+extern "C" xa_status_t xattn_mask_to_cache_blocks(const uint8_t* block_mask, int32_t heads,
+                                                  int32_t n_qb, int64_t n_cols, int64_t mask_head_stride,
+                                                  int64_t mask_row_stride, int64_t kb_begin,
+                                                  int64_t n_cache_blocks, int32_t sub_blocks,
+                                                  int32_t force_first_last, uint8_t* keep_per_head,
+                                                  uint8_t* keep_any, uint8_t* keep_any_blocks,
+                                                  xa_stream_t stream) {
+  using xa_host::fail;
+  if (heads <= 0 || n_qb <= 0 || sub_blocks <= 0 || n_cols <= 0 || kb_begin < 0 || n_cache_blocks < 0)
+    return fail(XA_EINVAL, "xattn_mask_to_cache_blocks: need heads, n_qb, sub_blocks, n_cols > 0 "
+                "and kb_begin, n_cache_blocks >= 0");
+  if (mask_head_stride < 0 || mask_row_stride < 0)
+    return fail(XA_EINVAL, "xattn_mask_to_cache_blocks: negative mask stride");
+  if (n_cache_blocks == 0) return XA_OK;
+  if (kb_begin + (n_cache_blocks - 1) * (int64_t)sub_blocks >= n_cols)
+    return fail(XA_EINVAL, "xattn_mask_to_cache_blocks: cache block %lld starts at column %lld >= n_cols %lld",
+                (long long)(n_cache_blocks - 1),
+                (long long)(kb_begin + (n_cache_blocks - 1) * (int64_t)sub_blocks), (long long)n_cols);
+  if (!block_mask) return fail(XA_EINVAL, "xattn_mask_to_cache_blocks: null block_mask");
+  if (!keep_per_head && !keep_any && !keep_any_blocks) return XA_OK;
+  if (n_cache_blocks > 0x7fffffff) return fail(XA_EUNSUPPORTED, "xattn_mask_to_cache_blocks: too many cache blocks");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(cache_block_kernel, dim3((unsigned)n_cache_blocks), dim3(256), 0, s, block_mask,
+                     heads, n_qb, n_cols, mask_head_stride, mask_row_stride, kb_begin, n_cache_blocks,
+                     sub_blocks, force_first_last, keep_per_head, keep_any, keep_any_blocks);
+  return xa_host::check_launch("xattn_mask_to_cache_blocks");
+}

@@ -1,0 +1,136 @@
+"""One attention layer's chunked prefill through the C ABI.
+
+XAttentionBSAPolicy (nano-vllm xattn_bsa.py page), select_blocks +
+compute_chunked_prefill: for the query chunk at global position p,
+  1. estimate block scores and the block mask against K[0 : p+C];
+  2. attend the history K/V[0 : p) without the causal rule, kept blocks only;
+  3. attend the chunk's own K/V[p : p+C) with the causal rule, kept blocks only;
+  4. merge the two partial results by their LSE.
+The cache-block variant first reduces the history part of the mask to
+1024-token cache blocks (union over heads and query blocks, first and last
+forced) and attends every 128-token block of the kept cache blocks, with
+dense causal attention inside the chunk.
+
+All buffers are allocated up front; a step only enqueues library calls on
+the current stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class ChunkBuffers:
+    p: int
+    scores: torch.Tensor
+    mask: torch.Tensor
+    o_hist: torch.Tensor | None
+    l_hist: torch.Tensor | None
+    o_cur: torch.Tensor
+    l_cur: torch.Tensor
+    lse: torch.Tensor
+    keep_per_head: torch.Tensor | None = None
+    keep_any: torch.Tensor | None = None
+    keep_any_blocks: torch.Tensor | None = None
+
+
+class ChunkedPrefill:
+    """Preallocated chunked prefill of one layer (batch 1).
+
+    q [L, Hq, d], k/v [L, Hkv, d] on the GPU.  ``chunk_starts`` selects which
+    chunks to run (default: all, in order).  ``cache_block`` switches the
+    history attention to the cache-block form.
+    """
+
+    def __init__(self, q, k, v, chunk: int, stride: int, threshold: float, block: int = 128,
+                 chunk_starts=None, cache_block: int | None = None, out_dtype=None):
+        self.q, self.k, self.v = q, k, v
+        self.L, self.hq, self.d = q.shape
+        self.hkv = k.shape[1]
+        self.chunk, self.stride, self.threshold, self.block = chunk, stride, threshold, block
+        self.cache_block = cache_block
+        dev = q.device
+        self.out_dtype = q.dtype if out_dtype is None else out_dtype
+        self.starts = list(range(0, self.L, chunk)) if chunk_starts is None else list(chunk_starts)
+        dt = B.XA_BF16 if q.dtype == torch.bfloat16 else B.XA_F32
+        max_k = max(p + min(chunk, self.L - p) for p in self.starts)
+        est_ws = max(B.xattn_estimate_workspace_size(min(chunk, self.L - p), p + min(chunk, self.L - p),
+                                                     self.hq, self.hkv, self.d, stride, block, dt)
+                     for p in self.starts)
+        bsa_ws = B.bsa_prefill_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
+        self.est_ws = B.workspace(est_ws, dev)
+        self.bsa_ws = B.workspace(bsa_ws, dev)
+        self.out = torch.empty(self.L, self.hq, self.d, dtype=self.out_dtype, device=dev)
+        self.bufs = []
+        for p in self.starts:
+            c = min(chunk, self.L - p)
+            nqb, nkb = c // block, (p + c) // block
+            hist = p > 0
+            kb = None
+            if hist and cache_block:
+                sub = cache_block // block
+                ncb = p // cache_block
+                kb = dict(keep_per_head=torch.empty(self.hq, nqb, ncb, dtype=torch.uint8, device=dev),
+                          keep_any=torch.empty(ncb, dtype=torch.uint8, device=dev),
+                          keep_any_blocks=torch.empty(ncb * sub, dtype=torch.uint8, device=dev))
+            self.bufs.append(ChunkBuffers(
+                p=p,
+                scores=torch.empty(self.hq, nqb, nkb, dtype=torch.float32, device=dev),
+                mask=torch.empty(self.hq, nqb, nkb, dtype=torch.uint8, device=dev),
+                o_hist=torch.empty(c, self.hq, self.d, dtype=self.out_dtype, device=dev) if hist else None,
+                l_hist=torch.empty(self.hq, c, dtype=torch.float32, device=dev) if hist else None,
+                o_cur=torch.empty(c, self.hq, self.d, dtype=self.out_dtype, device=dev) if hist else self.out[p:p + c],
+                l_cur=torch.empty(self.hq, c, dtype=torch.float32, device=dev),
+                lse=torch.empty(self.hq, c, dtype=torch.float32, device=dev),
+                **(kb or {})))
+
+    # -- the four calls of one chunk ------------------------------------------------
+    def estimate(self, b: ChunkBuffers):
+        c = b.scores.shape[1] * self.block
+        B.xattn_estimate(self.q[b.p:b.p + c], self.k[:b.p + c], b.p, self.stride, self.threshold, self.block,
+                         block_scores=b.scores, block_mask=b.mask, ws=self.est_ws)
+
+    def reduce(self, b: ChunkBuffers):
+        if b.keep_any is None:
+            return
+        ncb = b.keep_any.shape[0]
+        B.xattn_mask_to_cache_blocks(b.mask, 0, ncb, self.cache_block // self.block, True,
+                                     keep_per_head=b.keep_per_head, keep_any=b.keep_any,
+                                     keep_any_blocks=b.keep_any_blocks)
+
+    def attend(self, b: ChunkBuffers):
+        p = b.p
+        c = b.scores.shape[1] * self.block
+        qc = self.q[p:p + c]
+        if p > 0:
+            if b.keep_any_blocks is not None:
+                B.bsa_prefill(qc, self.k[:p], self.v[:p], p, 0, b.keep_any_blocks.view(1, 1, -1), 0, False,
+                              out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws, mask_head_stride=0, mask_row_stride=0)
+            else:
+                B.bsa_prefill(qc, self.k[:p], self.v[:p], p, 0, b.mask, 0, False,
+                              out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws)
+        cur_mask = None if b.keep_any_blocks is not None else b.mask
+        B.bsa_prefill(qc, self.k[p:p + c], self.v[p:p + c], p, p, cur_mask, 0, True,
+                      out=b.o_cur, lse=b.l_cur if p > 0 else b.lse, ws=self.bsa_ws)
+
+    def merge(self, b: ChunkBuffers):
+        if b.p == 0:
+            return
+        c = b.scores.shape[1] * self.block
+        B.attn_merge(b.o_hist, b.l_hist, b.o_cur, b.l_cur, o_out=self.out[b.p:b.p + c], lse_out=b.lse)
+
+    def run_chunk(self, i: int):
+        b = self.bufs[i]
+        self.estimate(b)
+        self.reduce(b)
+        self.attend(b)
+        self.merge(b)
+
+    def run(self):
+        for i in range(len(self.bufs)):
+            self.run_chunk(i)
+        return self.out

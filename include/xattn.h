@@ -1,0 +1,192 @@
+/*
+ * xattn.h -- C ABI of the MI355X (gfx950) XAttention block-sparse
+ * chunked-prefill library (libxattn.so).
+ *
+ * The path has three parts plus a mask reducer:
+ *   1. xattn_estimate          -- stride-S antidiagonal importance estimate and
+ *                                 cumulative-threshold block selection;
+ *   2. bsa_prefill             -- block-sparse flash attention over the kept
+ *                                 128-token blocks, returning out and LSE;
+ *   3. attn_merge              -- LSE merge of two partial attention results;
+ *   4. xattn_mask_to_cache_blocks -- 128-token block mask -> cache blocks.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors) unless a comment says otherwise.  The caller owns every buffer.
+ *     The library never allocates device memory, never frees caller memory
+ *     and never synchronises: every call only enqueues kernels on `stream`
+ *     (0 = the null stream) and returns.
+ *   - Token-major layouts as in the pages' varlen tensors: Q is
+ *     [q_len][num_q_heads][head_dim], K and V are [kv_len][num_kv_heads][head_dim],
+ *     addressed through element strides (token stride, head stride); the
+ *     head_dim axis must be contiguous.  Outputs are dense (layouts below).
+ *   - GQA: query head h reads key/value head h / (num_q_heads / num_kv_heads).
+ *   - Arguments are validated before anything is launched.  On a non-OK
+ *     status nothing has been enqueued and no output was written;
+ *     xattn_last_error() returns a thread-local message.  XA_EHIP means a
+ *     launch failed (hipGetLastError); outputs are then undefined.
+ *   - Batch = 1 per call (one sequence), as the policy on the pages does.
+ *   - Thread-safe: no global mutable state besides the thread-local message.
+ */
+#ifndef XATTN_H_
+#define XATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* xa_stream_t; /* a hipStream_t */
+
+typedef enum {
+  XA_OK = 0,
+  XA_EINVAL = 1,        /* bad pointer, size, stride or combination */
+  XA_EUNSUPPORTED = 2,  /* valid request outside what the kernels implement */
+  XA_EWORKSPACE = 3,    /* workspace missing or smaller than the size query */
+  XA_EHIP = 4           /* a HIP launch failed */
+} xa_status_t;
+
+typedef enum { XA_F32 = 0, XA_BF16 = 1 } xa_dtype_t;
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char* xattn_last_error(void);
+
+/* Library version string (static storage). */
+const char* xattn_version(void);
+
+/* ------------------------------------------------------------------------
+ * Part 1: importance estimate + block selection  (xattn_estimate_chunked)
+ *
+ * Follows the XAttention algorithm guide (nano-vllm docs): "Stride Reshape
+ * 详解 / Inverse 模式", "Triton Kernels 详解" (flat_group_gemm_fuse_reshape,
+ * softmax_fuse_block_sum) and "块选择算法 (find_blocks_chunked)", with the
+ * chunk placement of XAttentionBSAPolicy.select_blocks (nano-vllm
+ * xattn_bsa.py page).  For query chunk Q (global positions
+ * q_start_pos .. q_start_pos+q_len-1) against K rows 0 .. k_len-1
+ * (k_len == q_start_pos + q_len):
+ *   reshaped row r   = concat_t Q[r*S + S-1-t],  t = 0..S-1
+ *   reshaped column c = concat_t K[c*S + t]
+ *   z[r][c] = <row r, column c> / (S * sqrt(head_dim)), visible iff
+ *             c <= q_start_pos/S + r
+ *   P = row softmax over the visible columns
+ *   block_scores[h][qb][kb] = sum of P over the (block/S x block/S) tile
+ *   block_mask[h][qb][kb] = 1 for kb == 0 and kb == q_start_pos/block + qb
+ *     (always kept); the other kb <= that diagonal are ranked by score
+ *     (descending, ties by ascending kb) and kept while
+ *     (mass of the always-kept blocks + mass ranked before) < threshold * row
+ *     total; threshold >= 1 keeps every kb <= diagonal; kb > diagonal = 0.
+ *
+ * dtype: XA_BF16 (MFMA bf16 x bf16 -> fp32) or XA_F32 (each fp32 value is
+ *   split into bf16 hi + lo and three MFMA products are accumulated,
+ *   about 16 mantissa bits).
+ * Requirements: head_dim in {64, 128}; stride in {2, 4, 8, 16}; block == 128;
+ *   q_len, q_start_pos multiples of block; q_len > 0; k_len == q_start_pos + q_len;
+ *   k_len / block <= 8192; num_q_heads % num_kv_heads == 0.
+ * Outputs (dense, caller-allocated):
+ *   block_scores : float   [num_q_heads][q_len/block][k_len/block]
+ *   block_mask   : uint8_t [num_q_heads][q_len/block][k_len/block]
+ * Workspace: at least xattn_estimate_workspace_size(...) bytes of device
+ *   memory, 256-byte aligned; contents on entry are ignored.
+ * ------------------------------------------------------------------------ */
+size_t xattn_estimate_workspace_size(int64_t q_len, int64_t k_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t stride,
+                                     int32_t block, xa_dtype_t dtype);
+
+xa_status_t xattn_estimate(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                           const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                           xa_dtype_t dtype, int64_t q_len, int64_t k_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int64_t q_start_pos, int32_t stride, int32_t block, float threshold,
+                           float* block_scores, uint8_t* block_mask,
+                           void* workspace, size_t workspace_bytes, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Part 2: block-sparse flash attention with LSE  (block_sparse_attn_func /
+ * flash_attn_with_lse on the pages)
+ *
+ * XAttention algorithm guide, "BSA (Block Sparse Attention)"; the history /
+ * current-chunk split of XAttentionBSAPolicy.compute_chunked_prefill.
+ * K/V row j is global position kv_start + j.  Query row i (global
+ * q_start_pos + i) attends to key j iff
+ *   mask[h][i/block][(kv_start+j)/block - mask_kb_offset] != 0
+ *   and (causal == 0 or kv_start + j <= q_start_pos + i);
+ * with s = softmax_scale (0 => 1/sqrt(head_dim)):
+ *   lse[h][i] = ln sum_j exp(s q_i.k_j),  out[i][h] = sum_j exp(s q_i.k_j - lse) v_j.
+ * A row with no visible key gets out = 0 and lse = -inf.
+ * Mask addressing: byte at block_mask + h*mask_head_stride + qb*mask_row_stride + col;
+ *   strides may be 0 to broadcast one row to every head / query block;
+ *   block_mask == NULL keeps every block (dense).
+ * dtype: XA_BF16 (bf16 MFMA, fp32 softmax) or XA_F32 (split bf16 hi/lo, see above).
+ * Requirements: head_dim in {64, 128}; block == 128; q_len, q_start_pos,
+ *   kv_start multiples of block; kv_len > 0 (any length: the last block may be
+ *   partial); num_q_heads % num_kv_heads == 0.
+ * Outputs: out  : out_dtype [q_len][num_q_heads][head_dim] (XA_F32 or XA_BF16)
+ *          lse  : float [num_q_heads][q_len], natural log.
+ * Workspace: at least bsa_prefill_workspace_size(...) bytes (holds V
+ *   transposed per kv head, and for XA_F32 the bf16 hi/lo planes).
+ * ------------------------------------------------------------------------ */
+size_t bsa_prefill_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype);
+
+xa_status_t bsa_prefill(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                        const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                        const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                        xa_dtype_t dtype, int64_t q_len, int64_t kv_len,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int64_t q_start_pos, int64_t kv_start,
+                        const uint8_t* block_mask, int64_t mask_head_stride,
+                        int64_t mask_row_stride, int64_t mask_kb_offset,
+                        int32_t block, int32_t causal, float softmax_scale,
+                        void* out, xa_dtype_t out_dtype, float* lse,
+                        void* workspace, size_t workspace_bytes, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Part 3: LSE merge  (merge_attention_outputs)
+ *
+ * nano-vllm CLAUDE.md, "Online Softmax Merge - Triton Fused Kernel":
+ *   m = max(lse_a, lse_b); e_x = exp(lse_x - m);
+ *   lse_out = m + ln(e_a + e_b);  o_out = (o_a e_a + o_b e_b) / (e_a + e_b).
+ * Both lse = -inf gives o_out = 0, lse_out = -inf; one -inf returns the other.
+ * o_*: o_dtype [q_len][heads][head_dim] dense; lse_*: float [heads][q_len].
+ * Math in fp32.  o_out may alias o_a or o_b, lse_out may alias lse_a or lse_b
+ * (each element is read before it is written by the same thread).
+ * Requirements: q_len >= 0, heads > 0, head_dim > 0 and head_dim % 8 == 0.
+ * ------------------------------------------------------------------------ */
+xa_status_t attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                       void* o_out, float* lse_out, xa_dtype_t o_dtype,
+                       int64_t q_len, int32_t heads, int32_t head_dim, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * 128-token block mask -> cache blocks
+ *
+ * Task plan page (nano-vllm task_plan.md), "select_blocks 设计" step 3, and
+ * XAttentionBSAPolicy.select_blocks step 6: a cache block of sub_blocks
+ * consecutive 128-token blocks is kept if any of them is selected; the union
+ * over heads and query blocks is the list of cache blocks to load, with the
+ * first and last history cache block always included (force_first_last).
+ *   mask byte (h, qb, col) at block_mask + h*mask_head_stride + qb*mask_row_stride + col
+ *   cache block cb covers columns kb_begin + cb*sub_blocks .. (clipped to n_cols)
+ * Outputs (each may be NULL):
+ *   keep_per_head : uint8_t [heads][n_qb][n_cache_blocks]
+ *   keep_any      : uint8_t [n_cache_blocks]
+ *   keep_any_blocks : uint8_t [n_cache_blocks * sub_blocks] -- keep_any
+ *                     expanded back to 128-token columns (a broadcast mask
+ *                     row for bsa_prefill with zero head/row strides).
+ * Requirements: heads, n_qb, sub_blocks > 0; 0 <= kb_begin; n_cache_blocks >= 0;
+ *   kb_begin + (n_cache_blocks-1)*sub_blocks < n_cols when n_cache_blocks > 0.
+ * ------------------------------------------------------------------------ */
+xa_status_t xattn_mask_to_cache_blocks(const uint8_t* block_mask, int32_t heads, int32_t n_qb,
+                                       int64_t n_cols, int64_t mask_head_stride,
+                                       int64_t mask_row_stride, int64_t kb_begin,
+                                       int64_t n_cache_blocks, int32_t sub_blocks,
+                                       int32_t force_first_last, uint8_t* keep_per_head,
+                                       uint8_t* keep_any, uint8_t* keep_any_blocks,
+                                       xa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H_ */

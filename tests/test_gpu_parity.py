@@ -1,0 +1,188 @@
+"""GPU parity: every entry point of libxattn.so against the CPU oracle.
+
+Inputs are seeded; the oracle runs in float64 on exactly the values the GPU
+sees (bf16 inputs are rounded once on the host, then upcast).  Shapes span
+several tiles and ragged tails (partial key blocks, empty rows, GQA groups of
+1, 2, 4 and 7).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import xattn_oracle as O
+from tests import parity as PAR
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from block_sparse_attention_xattn_amd import binding
+    binding.lib()  # raises if the library is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+
+
+def _np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def _rand(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn(*shape, generator=g)).to(dtype)
+
+
+# --------------------------------------------------------------------------- merge
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("q_len,heads,d", [(256, 4, 128), (384, 3, 64), (1, 1, 8), (128, 2, 96)])
+def test_merge(dtype, q_len, heads, d):
+    from block_sparse_attention_xattn_amd import binding as B
+    oa = _rand((q_len, heads, d), dtype, 1)
+    ob = _rand((q_len, heads, d), dtype, 2)
+    la = _rand((heads, q_len), torch.float32, 3, 4.0)
+    lb = _rand((heads, q_len), torch.float32, 4, 4.0)
+    la.view(-1)[::7] = -float("inf")
+    lb.view(-1)[::5] = -float("inf")
+    ro, rl = O.merge(_np(oa), _np(la), _np(ob), _np(lb))
+    go, gl = B.attn_merge(oa.to(DEV), la.to(DEV), ob.to(DEV), lb.to(DEV))
+    torch.cuda.synchronize()
+    tol = PAR.OUT_ATOL_BF16 if dtype == torch.bfloat16 else 1e-5
+    PAR.check_out_lse(_np(go), _np(gl), ro, rl, tol)
+    # in place: out aliases o_a, lse_out aliases lse_a
+    ia, il = oa.to(DEV), la.to(DEV)
+    B.attn_merge(ia, il, ob.to(DEV), lb.to(DEV), o_out=ia, lse_out=il)
+    torch.cuda.synchronize()
+    PAR.check_out_lse(_np(ia), _np(il), ro, rl, tol)
+
+
+# --------------------------------------------------------------------------- reducer
+@pytest.mark.parametrize("seed,H,nqb,ncols,kb_begin,sub,force", [
+    (0, 32, 32, 992, 0, 8, True), (1, 4, 3, 37, 0, 8, True), (2, 2, 5, 40, 3, 4, False), (3, 1, 1, 8, 0, 8, True)])
+def test_reducer(seed, H, nqb, ncols, kb_begin, sub, force):
+    from block_sparse_attention_xattn_amd import binding as B
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((H, nqb, ncols)) < 0.02).astype(np.uint8)
+    ncb = (ncols - kb_begin + sub - 1) // sub
+    rp, ra = O.mask_to_cache_blocks(mask, kb_begin, ncb, sub, force)
+    gp, ga, gb = B.xattn_mask_to_cache_blocks(torch.from_numpy(mask).to(DEV), kb_begin, ncb, sub, force)
+    torch.cuda.synchronize()
+    assert np.array_equal(gp.cpu().numpy(), rp)
+    assert np.array_equal(ga.cpu().numpy(), ra)
+    assert np.array_equal(gb.cpu().numpy(), O.expand_cache_keep(ra, sub, ncb * sub))
+
+
+# --------------------------------------------------------------------------- bsa
+BSA_CASES = [
+    # hq, hkv, d, dtype, q_len, q_start, kv_start, kv_len, causal, density, seed
+    (2, 1, 64, torch.float32, 256, 0, 0, 256, True, 1.0, 0),
+    (4, 2, 128, torch.bfloat16, 384, 256, 0, 640, True, 0.5, 1),
+    (4, 1, 128, torch.bfloat16, 256, 512, 0, 512, False, 0.4, 2),
+    (7, 1, 128, torch.bfloat16, 256, 384, 384, 256, True, 0.6, 3),
+    (2, 2, 64, torch.bfloat16, 128, 1024, 128, 901, False, 0.5, 4),   # ragged key tail
+    (8, 4, 128, torch.float32, 256, 128, 0, 384, True, 0.5, 5),
+    (4, 4, 128, torch.bfloat16, 512, 0, 0, 512, True, 0.0, 6),       # only forced-free empty rows
+]
+
+
+def _bsa_case(hq, hkv, d, dtype, q_len, q_start, kv_start, kv_len, causal, density, seed):
+    from block_sparse_attention_xattn_amd import binding as B
+    q = _rand((q_len, hq, d), dtype, 10 + seed)
+    k = _rand((kv_len, hkv, d), dtype, 20 + seed)
+    v = _rand((kv_len, hkv, d), dtype, 30 + seed)
+    ncols = (kv_start + kv_len + 127) // 128
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((hq, q_len // 128, ncols)) < density).astype(np.uint8)
+    ro, rl = O.bsa(_np(q), _np(k), _np(v), q_start, kv_start, mask, 0, causal, None, 128)
+    go, gl = B.bsa_prefill(q.to(DEV), k.to(DEV), v.to(DEV), q_start, kv_start, torch.from_numpy(mask).to(DEV),
+                           0, causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tol = PAR.OUT_ATOL_BF16 if dtype == torch.bfloat16 else PAR.OUT_ATOL_F32
+    return PAR.check_out_lse(_np(go), _np(gl), ro, rl, tol)
+
+
+@pytest.mark.parametrize("case", BSA_CASES, ids=[f"bsa{i}" for i in range(len(BSA_CASES))])
+def test_bsa(case):
+    _bsa_case(*case)
+
+
+def test_bsa_dense_and_broadcast_mask():
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, q_len, p = 4, 2, 128, 256, 512
+    q = _rand((q_len, hq, d), torch.bfloat16, 40)
+    k = _rand((p, hkv, d), torch.bfloat16, 41)
+    v = _rand((p, hkv, d), torch.bfloat16, 42)
+    row = np.array([1, 0, 0, 1], dtype=np.uint8)
+    full = np.broadcast_to(row, (hq, q_len // 128, 4)).copy()
+    ro, rl = O.bsa(_np(q), _np(k), _np(v), p, 0, full, 0, False)
+    go, gl = B.bsa_prefill(q.to(DEV), k.to(DEV), v.to(DEV), p, 0, torch.from_numpy(row).to(DEV).view(1, 1, -1), 0,
+                           False, out_dtype=torch.float32, mask_head_stride=0, mask_row_stride=0)
+    torch.cuda.synchronize()
+    PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
+    ro, rl = O.bsa(_np(q), _np(k), _np(v), p, 0, None, 0, False)
+    go, gl = B.bsa_prefill(q.to(DEV), k.to(DEV), v.to(DEV), p, 0, None, 0, False)
+    torch.cuda.synchronize()
+    PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
+
+
+# --------------------------------------------------------------------------- estimate
+EST_CASES = [
+    # hq, hkv, d, dtype, q_len, q_start, stride, threshold, seed
+    (2, 1, 64, torch.float32, 1024, 0, 8, 0.9, 0),
+    (4, 2, 128, torch.bfloat16, 512, 512, 8, 0.95, 1),
+    (4, 1, 128, torch.bfloat16, 256, 768, 16, 0.9, 2),
+    (2, 2, 128, torch.bfloat16, 384, 128, 4, 0.8, 3),
+    (2, 1, 64, torch.bfloat16, 256, 256, 2, 0.9, 4),
+    (7, 1, 128, torch.bfloat16, 256, 1792, 8, 1.0, 5),
+    (4, 2, 64, torch.float32, 640, 1280, 8, 0.5, 6),
+]
+
+
+@pytest.mark.parametrize("case", EST_CASES, ids=[f"est{i}" for i in range(len(EST_CASES))])
+def test_estimate(case):
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, dtype, q_len, p, S, tau, seed = case
+    k_len = p + q_len
+    q = _rand((q_len, hq, d), dtype, 50 + seed)
+    k = _rand((k_len, hkv, d), dtype, 60 + seed)
+    rs, rm = O.estimate(_np(q), _np(k), p, S, tau)
+    gs, gm = B.xattn_estimate(q.to(DEV), k.to(DEV), p, S, tau)
+    torch.cuda.synchronize()
+    PAR.check_scores(gs.cpu().numpy(), rs)
+    PAR.check_mask(gm.cpu().numpy(), rs, rm, p, tau)
+
+
+# --------------------------------------------------------------------------- composed
+def test_tiny_chunked_prefill_end_to_end():
+    """The 1K fp32 workload: 2 query heads sharing 1 kv head, d 64, stride 8, threshold 0.9."""
+    from block_sparse_attention_xattn_amd import synthetic
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
+    q, k, v = synthetic.tiny(0)
+    ref = O.chunk_prefill(_np(q), _np(k), _np(v), 0, 8, 0.9)
+    run = ChunkedPrefill(q.to(DEV), k.to(DEV), v.to(DEV), chunk=1024, stride=8, threshold=0.9)
+    out = run.run()
+    torch.cuda.synchronize()
+    b = run.bufs[0]
+    PAR.check_scores(b.scores.cpu().numpy(), ref["scores"])
+    n_diff, _ = PAR.check_mask(b.mask.cpu().numpy(), ref["scores"], ref["mask"], 0, 0.9)
+    assert n_diff == 0
+    PAR.check_out_lse(_np(out), _np(b.lse), ref["out"], ref["lse"], PAR.OUT_ATOL_F32)
+
+
+def test_small_multichunk_prefill_end_to_end():
+    from block_sparse_attention_xattn_amd import synthetic
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
+    q, k, v = synthetic.long_context(4096, 8, 2, 128, n_needles=4, seed=7)
+    ref = O.chunked_prefill(_np(q), _np(k), _np(v), 1024, 8, 0.9)
+    run = ChunkedPrefill(q.to(DEV), k.to(DEV), v.to(DEV), chunk=1024, stride=8, threshold=0.9)
+    out = run.run()
+    torch.cuda.synchronize()
+    same = True
+    for i, b in enumerate(run.bufs):
+        PAR.check_scores(b.scores.cpu().numpy(), ref["scores"][i])
+        n_diff, _ = PAR.check_mask(b.mask.cpu().numpy(), ref["scores"][i], ref["masks"][i], b.p, 0.9)
+        same &= n_diff == 0
+    if same:
+        PAR.check_out_lse(_np(out), np.concatenate([_np(b.lse) for b in run.bufs], axis=1), ref["out"], ref["lse"],
+                          PAR.OUT_ATOL_BF16)
