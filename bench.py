@@ -1,0 +1,237 @@
+"""Benchmark: XAttention block-sparse chunked prefill of one attention layer on one MI355X.
+
+Step = the whole hot path over one layer's prefill: for every 4096-token
+chunk, pack the chunk's V rows, estimate block scores and the block mask,
+block-sparse attention over the history and over the chunk, LSE merge.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line.  Extra fields: per-part times, mask density,
+effective TFLOP/s on computed blocks, the attention kernel's roofline entry
+(HIP events around every attention launch in the timed region) and the CPU
+oracle timed on one key/value-head group of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b_32k_8x4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=1, help="kv-head groups timed for the CPU baseline")
+    return ap.parse_args()
+
+
+def count_flops(run):
+    """Algorithmic work of one step from the step's own block masks.
+
+    attention: 4*d*128^2 flop per computed (head, query block, key block) tile
+    (QK^T and PV), diagonal tiles counted whole; estimate: 2*(d*S) flop per
+    visible (reshaped row, reshaped column) pair.
+    Returns (bsa_flops_per_launch list in launch order, estimate_flops, density).
+    """
+    import numpy as np
+    d, S, blk = run.d, run.stride, run.block
+    per_tile = 4.0 * d * blk * blk
+    launches = []
+    est = 0.0
+    sel = tot = 0
+    for b in run.bufs:
+        m = b.mask.cpu().numpy().astype(bool)
+        hq, nqb, nkb = m.shape
+        cur = b.p // blk
+        if b.p > 0:
+            if b.keep_any_blocks is not None:
+                kept = int(b.keep_any_blocks.cpu().numpy().astype(bool).sum())
+                launches.append(per_tile * kept * hq * nqb)
+            else:
+                launches.append(per_tile * float(m[:, :, :cur].sum()))
+        if b.keep_any_blocks is not None:
+            launches.append(per_tile * hq * nqb * (nqb + 1) / 2)
+        else:
+            launches.append(per_tile * float(m[:, :, cur:].sum()))
+        causal = np.arange(nkb)[None, :] <= (cur + np.arange(nqb))[:, None]
+        sel += int((m & causal[None]).sum())
+        tot += int(causal.sum()) * hq
+        R = nqb * blk // S
+        cdiag = b.p // S
+        vis = float(np.sum(cdiag + np.arange(R) + 1))
+        est += 2.0 * d * S * vis * hq
+    return launches, est, sel / max(tot, 1)
+
+
+def cpu_baseline(name, groups):
+    """Time the oracle on `groups` kv-head groups of the workload (all chunks)."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_xattn_amd import synthetic
+    from oracle import xattn_oracle as O
+    w = synthetic.WORKLOADS[name]
+    q, k, v = synthetic.workload_inputs(name)
+    g = w["hq"] // w["hkv"]
+    hs = list(range(groups * g))
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    qs, ks, vs = f(q[:, hs]), f(k[:, :groups]), f(v[:, :groups])
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    O.chunked_prefill(qs, ks, vs, w["chunk"], w["stride"], w["threshold"])
+    dt = time.perf_counter() - t0
+    frac = groups / w["hkv"]
+    value = w["L"] * frac / dt
+    return {"value": round(value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle, all {w['L'] // w['chunk']} chunks of the {w['L']}-token layer for "
+                      f"{groups} of {w['hkv']} kv-head groups ({len(hs)} of {w['hq']} query heads); "
+                      f"tokens/s scaled by the head fraction (heads are independent); {dt:.1f} s of CPU time"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
+                                   "this build (the path shards by kv-head group, see DESIGN.md)",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_xattn_amd import synthetic
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
+
+    w = synthetic.WORKLOADS[a.workload]
+    dev = "cuda:0"
+    q, k, v = synthetic.workload_inputs(a.workload)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    starts = None
+    if "q_start_pos" in w:
+        starts = [w["q_start_pos"]]
+    run = ChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
+                         chunk_starts=starts, cache_block=w.get("cache_block"))
+    run.pack_history()
+    torch.cuda.synchronize()
+    for _ in range(a.warmup):
+        run.run()
+    torch.cuda.synchronize()
+
+    # timed region, with events around every library call
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def mark(tag):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.append((tag, e))
+
+    orig_attend, orig_est, orig_merge, orig_pack = run.attend, run.estimate, run.merge, run.pack
+
+    def timed(tag, fn):
+        def inner(b):
+            mark(tag + ":start")
+            fn(b)
+            mark(tag + ":end")
+        return inner
+
+    from block_sparse_attention_xattn_amd import binding as B
+    orig_bsa = B.bsa_prefill_packed
+
+    def bsa_timed(*args, **kw):
+        mark("bsa_launch:start")
+        r = orig_bsa(*args, **kw)
+        mark("bsa_launch:end")
+        return r
+
+    run.estimate = timed("estimate", orig_est)
+    run.merge = timed("merge", orig_merge)
+    run.pack = timed("pack", orig_pack)
+    B.bsa_prefill_packed = bsa_timed
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        run.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.bsa_prefill_packed = orig_bsa
+    gpu_ms = e0.elapsed_time(e1)
+    step_ms = max(gpu_ms, wall * 1e3) / a.steps
+
+    parts = {}
+    bsa_durs = []
+    open_ev = {}
+    for tag, e in ev:
+        name, kind = tag.split(":")
+        if kind == "start":
+            open_ev[name] = e
+        else:
+            dt = open_ev.pop(name).elapsed_time(e)
+            parts[name] = parts.get(name, 0.0) + dt
+            if name == "bsa_launch":
+                bsa_durs.append(dt)
+    for kk in parts:
+        parts[kk] /= a.steps
+
+    launches, est_flops, dens = count_flops(run)
+    bsa_flops_step = sum(launches)
+    n_launch = len(launches)
+    assert len(bsa_durs) == n_launch * a.steps, (len(bsa_durs), n_launch)
+    bsa_avg_ms = sum(bsa_durs) / len(bsa_durs)
+    bsa_tflops = (bsa_flops_step * a.steps) / (sum(bsa_durs) * 1e-3) / 1e12
+    eff_tflops = (bsa_flops_step + est_flops) / (step_ms * 1e-3) / 1e12
+    tokens = len(run.starts) * w["chunk"]
+    value = tokens / (step_ms * 1e-3)
+
+    out = {
+        "metric": "sparse prefill tokens/s per layer (estimate+BSA) at 32K/128K; % bf16 MFMA peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
+                   "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
+                   "block": 128, "chunks_timed": len(run.starts)},
+        "roofline": {"bound": "mfma", "kernel": "bsa_kernel (block-sparse attention)",
+                     "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(bsa_avg_ms, 4), "launches_per_step": n_launch,
+                     "flop_per_launch_avg": bsa_flops_step / n_launch},
+        "effective_tflops": round(eff_tflops, 1),
+        "effective_frac_of_peak": round(eff_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "density": round(dens, 4),
+        "parts_ms": {k2: round(v2, 3) for k2, v2 in parts.items()},
+        "estimate_gflop": round(est_flops / 1e9, 1),
+        "bsa_gflop": round(bsa_flops_step / 1e9, 1),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,15 @@ def _declare(lib):
     lib.bsa_prefill.restype = ctypes.c_int
     lib.bsa_prefill.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
                                 I64, I64, P, I64, I64, I64, I32, I32, F, P, ctypes.c_int, P, P, SZ, P]
+    lib.bsa_packed_v_bytes.restype = SZ
+    lib.bsa_packed_v_bytes.argtypes = [I64, I32, I32, ctypes.c_int]
+    lib.bsa_pack_v.restype = ctypes.c_int
+    lib.bsa_pack_v.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I32, P, I64, I64, P]
+    lib.bsa_prefill_packed_workspace_size.restype = SZ
+    lib.bsa_prefill_packed_workspace_size.argtypes = [I64, I64, I32, I32, I32, ctypes.c_int]
+    lib.bsa_prefill_packed.restype = ctypes.c_int
+    lib.bsa_prefill_packed.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
+                                       I64, I64, P, I64, I64, I64, I32, I32, F, P, ctypes.c_int, P, P, SZ, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -169,6 +178,66 @@ def bsa_prefill(q, k, v, q_start_pos: int, kv_start: int, block_mask=None, mask_
                              q_start_pos, kv_start, _ptr(block_mask), hs, rs, mask_kb_offset, block,
                              1 if causal else 0, float(softmax_scale), _ptr(out), odt, _ptr(lse),
                              _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def bsa_packed_v_bytes(capacity, num_kv_heads, head_dim, dtype=XA_BF16) -> int:
+    return int(lib().bsa_packed_v_bytes(capacity, num_kv_heads, head_dim, dtype))
+
+
+def bsa_prefill_packed_workspace_size(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype=XA_BF16) -> int:
+    return int(lib().bsa_prefill_packed_workspace_size(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype))
+
+
+class PackedV:
+    """A packed-V buffer of ``capacity`` tokens (see bsa_pack_v in xattn.h)."""
+
+    def __init__(self, capacity: int, num_kv_heads: int, head_dim: int, dtype, device):
+        self.capacity, self.hkv, self.d = capacity, num_kv_heads, head_dim
+        self.dtype = dtype
+        self.code = _dtype_code(torch.empty(0, dtype=dtype))
+        self.buf = workspace(bsa_packed_v_bytes(capacity, num_kv_heads, head_dim, self.code), device)
+
+
+def bsa_pack_v(v, packed: PackedV, token_offset: int, stream=None):
+    """Pack V rows [n, Hkv, d] as packed tokens token_offset .. token_offset+n-1."""
+    _qkv_check(v, "v")
+    if v.dtype != packed.dtype:
+        raise XattnError(XA_EINVAL, "v dtype differs from the packed buffer")
+    n, hkv, d = v.shape
+    _check(lib().bsa_pack_v(_ptr(v), v.stride(0), v.stride(1), packed.code, n, hkv, d, _ptr(packed.buf),
+                            packed.capacity, token_offset, _stream(stream)))
+
+
+def bsa_prefill_packed(q, k, packed: PackedV, v_token_offset: int, q_start_pos: int, kv_start: int,
+                       block_mask=None, mask_kb_offset: int = 0, causal: bool = True, softmax_scale: float = 0.0,
+                       out_dtype=None, block: int = 128, out=None, lse=None, ws=None, mask_head_stride=None,
+                       mask_row_stride=None, stream=None):
+    """bsa_prefill with V read from packed tokens v_token_offset .. +kv_len.  Returns (out, lse)."""
+    for t, nm in ((q, "q"), (k, "k")):
+        _qkv_check(t, nm)
+    dt = _dtype_code(q)
+    q_len, hq, d = q.shape
+    kv_len, hkv, _ = k.shape
+    if out_dtype is None:
+        out_dtype = q.dtype
+    odt = _dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty(q_len, hq, d, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(hq, q_len, dtype=torch.float32, device=q.device)
+    hs = rs = 0
+    if block_mask is not None:
+        hs = block_mask.stride(0) if mask_head_stride is None else mask_head_stride
+        rs = block_mask.stride(1) if mask_row_stride is None else mask_row_stride
+    need = bsa_prefill_packed_workspace_size(q_len, kv_len, hq, hkv, d, dt)
+    if ws is None and need > 0:
+        ws = workspace(need, q.device)
+    _check(lib().bsa_prefill_packed(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+                                    _ptr(packed.buf), packed.capacity, v_token_offset, dt, q_len, kv_len, hq, hkv,
+                                    d, q_start_pos, kv_start, _ptr(block_mask), hs, rs, mask_kb_offset, block,
+                                    1 if causal else 0, float(softmax_scale), _ptr(out), odt, _ptr(lse), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
 
 

@@ -202,67 +202,40 @@ extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_he
 }
 
 // ---------------------------------------------------------------------------
-// bsa_prefill
+// packed V and bsa_prefill / bsa_prefill_packed
 // ---------------------------------------------------------------------------
 namespace {
-struct BsaLayout {
-  size_t vh_off, vl_off, qh_off, ql_off, kh_off, kl_off, total;
-  int64_t pitch;
-};
+int64_t packed_pitch(int64_t capacity) { return (capacity + 127) / 128 * 128; }
 
-BsaLayout bsa_layout(int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, xa_dtype_t dt) {
-  BsaLayout L{};
-  L.pitch = (kv_len + 127) / 128 * 128;
-  const size_t vt = align256((size_t)hkv * d * L.pitch * 2);
-  size_t off = 0;
-  L.vh_off = off;
-  off += vt;
-  if (dt == XA_F32) {
-    L.vl_off = off;
-    off += vt;
-    const size_t pq = align256((size_t)q_len * hq * d * 2);
-    const size_t pk = align256((size_t)kv_len * hkv * d * 2);
-    L.qh_off = off;
-    off += pq;
-    L.ql_off = off;
-    off += pq;
-    L.kh_off = off;
-    off += pk;
-    L.kl_off = off;
-    off += pk;
-  }
-  L.total = off;
-  return L;
-}
-}  // namespace
-
-extern "C" size_t bsa_prefill_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
-                                             int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype) {
-  if (q_len <= 0 || kv_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  return bsa_layout(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype).total;
+size_t packed_bytes(int64_t capacity, int32_t hkv, int32_t d, xa_dtype_t dt) {
+  const size_t planes = dt == XA_F32 ? 2 : 1;
+  return align256(planes * (size_t)hkv * d * packed_pitch(capacity) * 2);
 }
 
-extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
-                                   int64_t k_head, const void* v, int64_t v_tok, int64_t v_head, xa_dtype_t dtype,
-                                   int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d,
-                                   int64_t q_start, int64_t kv_start, const uint8_t* block_mask,
-                                   int64_t mask_hs, int64_t mask_rs, int64_t mask_off, int32_t block,
-                                   int32_t causal, float softmax_scale, void* out, xa_dtype_t out_dtype,
-                                   float* lse, void* workspace, size_t ws_bytes, xa_stream_t stream) {
-  const char* fn = "bsa_prefill";
+// fp32 query/key planes (bf16 hi + lo) needed by the split path.
+size_t split_qk_bytes(int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, xa_dtype_t dt) {
+  if (dt != XA_F32) return 0;
+  return 2 * align256((size_t)q_len * hq * d * 2) + 2 * align256((size_t)kv_len * hkv * d * 2);
+}
+
+xa_status_t validate_bsa_common(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k,
+                                int64_t k_tok, int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t kv_len,
+                                int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int64_t kv_start,
+                                const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs, int64_t mask_off,
+                                int32_t block, float softmax_scale, void* out, xa_dtype_t out_dtype, float* lse) {
   xa_status_t st;
   if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
   if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
   if (out_dtype != XA_F32 && out_dtype != XA_BF16)
     return fail(XA_EUNSUPPORTED, "%s: out_dtype must be XA_F32 or XA_BF16", fn);
   if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
-  if (q_len <= 0 || q_len % block != 0) return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of %d", fn, (long long)q_len, block);
+  if (q_len <= 0 || q_len % block != 0)
+    return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of %d", fn, (long long)q_len, block);
   if (kv_len <= 0) return fail(XA_EINVAL, "%s: kv_len must be positive", fn);
   if (q_start < 0 || q_start % block != 0 || kv_start < 0 || kv_start % block != 0)
     return fail(XA_EINVAL, "%s: q_start_pos and kv_start must be non-negative multiples of %d", fn, block);
   if ((st = check_tensor(fn, "q", q, q_tok, q_head, q_len, hq, d, dtype)) != XA_OK) return st;
   if ((st = check_tensor(fn, "k", k, k_tok, k_head, kv_len, hkv, d, dtype)) != XA_OK) return st;
-  if ((st = check_tensor(fn, "v", v, v_tok, v_head, kv_len, hkv, d, dtype)) != XA_OK) return st;
   if (block_mask && (mask_hs < 0 || mask_rs < 0)) return fail(XA_EINVAL, "%s: negative mask stride", fn);
   if (block_mask && kv_start / block - mask_off < 0)
     return fail(XA_EINVAL, "%s: mask_kb_offset %lld is past the first key block %lld", fn, (long long)mask_off,
@@ -270,15 +243,17 @@ extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head,
   if (!out || !lse) return fail(XA_EINVAL, "%s: out and lse are required", fn);
   if ((uintptr_t)out % 16 != 0) return fail(XA_EINVAL, "%s: out must be 16-byte aligned", fn);
   if (!(softmax_scale >= 0.f)) return fail(XA_EINVAL, "%s: softmax_scale must be >= 0 (0 = 1/sqrt(d))", fn);
-  const BsaLayout L = bsa_layout(q_len, kv_len, hq, hkv, d, dtype);
-  if (!workspace || ws_bytes < L.total || (uintptr_t)workspace % 256 != 0)
-    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, L.total,
-                ws_bytes);
-  const int64_t n_qb = q_len / block;
-  if ((int64_t)hq * n_qb > 0x7fffffff) return fail(XA_EUNSUPPORTED, "%s: grid too large", fn);
+  if ((int64_t)hq * (q_len / block) > 0x7fffffff) return fail(XA_EUNSUPPORTED, "%s: grid too large", fn);
+  return XA_OK;
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+// Launch the attention kernel once the packed V (hi/lo planes) is in place.
+xa_status_t bsa_launch(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                       int64_t k_head, const bf16* vt_hi, const bf16* vt_lo, int64_t pitch, xa_dtype_t dtype,
+                       int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, int64_t q_start,
+                       int64_t kv_start, const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs,
+                       int64_t mask_off, int32_t block, int32_t causal, float softmax_scale, void* out,
+                       xa_dtype_t out_dtype, float* lse, char* split_ws, hipStream_t s) {
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   BsaParams p{};
   p.q_len = q_len;
@@ -286,7 +261,7 @@ extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head,
   p.hq = hq;
   p.hkv = hkv;
   p.group = hq / hkv;
-  p.n_qb = (int)n_qb;
+  p.n_qb = (int)(q_len / block);
   p.q_start = q_start;
   p.kv_start = kv_start;
   p.mask = block_mask;
@@ -297,14 +272,11 @@ extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head,
   p.scale_log2 = scale * kLog2e;
   p.out = out;
   p.lse = lse;
-  p.vt_pitch = L.pitch;
-  p.vt_head = (int64_t)d * L.pitch;
-  bf16* vh = reinterpret_cast<bf16*>(ws + L.vh_off);
-  bf16* vl = dtype == XA_F32 ? reinterpret_cast<bf16*>(ws + L.vl_off) : nullptr;
-  hipError_t e = launch_vt(v, dtype, v_tok, v_head, kv_len, hkv, d, vh, vl, L.pitch, s);
-  if (e != hipSuccess) return fail(XA_EHIP, "%s: V transpose launch failed: %s", fn, hipGetErrorString(e));
-  p.vt_hi = vh;
-  p.vt_lo = vl;
+  p.vt_pitch = pitch;
+  p.vt_head = (int64_t)d * pitch;
+  p.vt_hi = vt_hi;
+  p.vt_lo = vt_lo;
+  hipError_t e;
   if (dtype == XA_BF16) {
     p.q_hi = static_cast<const bf16*>(q);
     p.k_hi = static_cast<const bf16*>(k);
@@ -313,10 +285,12 @@ extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head,
     p.k_tok = k_tok;
     p.k_head = k_head;
   } else {
-    bf16* qh = reinterpret_cast<bf16*>(ws + L.qh_off);
-    bf16* ql = reinterpret_cast<bf16*>(ws + L.ql_off);
-    bf16* kh = reinterpret_cast<bf16*>(ws + L.kh_off);
-    bf16* kl = reinterpret_cast<bf16*>(ws + L.kl_off);
+    const size_t pq = align256((size_t)q_len * hq * d * 2);
+    const size_t pk = align256((size_t)kv_len * hkv * d * 2);
+    bf16* qh = reinterpret_cast<bf16*>(split_ws);
+    bf16* ql = reinterpret_cast<bf16*>(split_ws + pq);
+    bf16* kh = reinterpret_cast<bf16*>(split_ws + 2 * pq);
+    bf16* kl = reinterpret_cast<bf16*>(split_ws + 2 * pq + pk);
     if ((e = launch_split((const float*)q, q_tok, q_head, q_len, hq, d, qh, ql, s)) != hipSuccess ||
         (e = launch_split((const float*)k, k_tok, k_head, kv_len, hkv, d, kh, kl, s)) != hipSuccess)
       return fail(XA_EHIP, "%s: split launch failed: %s", fn, hipGetErrorString(e));
@@ -340,4 +314,108 @@ extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head,
   }
   if (e != hipSuccess) return fail(XA_EHIP, "%s: attention launch failed: %s", fn, hipGetErrorString(e));
   return XA_OK;
+}
+}  // namespace
+
+extern "C" size_t bsa_packed_v_bytes(int64_t capacity, int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype) {
+  if (capacity <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return packed_bytes(capacity, num_kv_heads, head_dim, dtype);
+}
+
+extern "C" xa_status_t bsa_pack_v(const void* v, int64_t v_tok, int64_t v_head, xa_dtype_t dtype, int64_t n_tokens,
+                                  int32_t hkv, int32_t d, void* packed_v, int64_t capacity, int64_t token_offset,
+                                  xa_stream_t stream) {
+  const char* fn = "bsa_pack_v";
+  xa_status_t st;
+  if ((st = check_heads(fn, hkv, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
+  if (n_tokens <= 0 || capacity <= 0) return fail(XA_EINVAL, "%s: n_tokens and capacity must be positive", fn);
+  if (token_offset < 0 || token_offset % 128 != 0)
+    return fail(XA_EINVAL, "%s: token_offset must be a non-negative multiple of 128", fn);
+  const int64_t pitch = packed_pitch(capacity);
+  if (token_offset + (n_tokens + 127) / 128 * 128 > pitch)
+    return fail(XA_EINVAL, "%s: tokens [%lld, %lld) exceed the packed capacity %lld", fn, (long long)token_offset,
+                (long long)(token_offset + n_tokens), (long long)pitch);
+  if ((st = check_tensor(fn, "v", v, v_tok, v_head, n_tokens, hkv, d, dtype)) != XA_OK) return st;
+  if (!packed_v || (uintptr_t)packed_v % 256 != 0) return fail(XA_EINVAL, "%s: packed_v must be 256-byte aligned", fn);
+  bf16* vh = static_cast<bf16*>(packed_v);
+  bf16* vl = dtype == XA_F32 ? vh + (size_t)hkv * d * pitch : nullptr;
+  const hipError_t e = launch_vt(v, dtype, v_tok, v_head, n_tokens, hkv, d, vh, vl, pitch, token_offset,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return XA_OK;
+}
+
+extern "C" size_t bsa_prefill_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype) {
+  if (q_len <= 0 || kv_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return packed_bytes(kv_len, num_kv_heads, head_dim, dtype) +
+         split_qk_bytes(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype);
+}
+
+extern "C" size_t bsa_prefill_packed_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype) {
+  if (q_len <= 0 || kv_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return split_qk_bytes(q_len, kv_len, num_q_heads, num_kv_heads, head_dim, dtype);
+}
+
+extern "C" xa_status_t bsa_prefill(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                                   int64_t k_head, const void* v, int64_t v_tok, int64_t v_head, xa_dtype_t dtype,
+                                   int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                                   int64_t q_start, int64_t kv_start, const uint8_t* block_mask,
+                                   int64_t mask_hs, int64_t mask_rs, int64_t mask_off, int32_t block,
+                                   int32_t causal, float softmax_scale, void* out, xa_dtype_t out_dtype,
+                                   float* lse, void* workspace, size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "bsa_prefill";
+  xa_status_t st = validate_bsa_common(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, kv_len, hq, hkv, d,
+                                       q_start, kv_start, block_mask, mask_hs, mask_rs, mask_off, block,
+                                       softmax_scale, out, out_dtype, lse);
+  if (st != XA_OK) return st;
+  if ((st = check_tensor(fn, "v", v, v_tok, v_head, kv_len, hkv, d, dtype)) != XA_OK) return st;
+  const size_t need = bsa_prefill_workspace_size(q_len, kv_len, hq, hkv, d, dtype);
+  if (!workspace || ws_bytes < need || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                ws_bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t pitch = packed_pitch(kv_len);
+  bf16* vh = reinterpret_cast<bf16*>(ws);
+  bf16* vl = dtype == XA_F32 ? vh + (size_t)hkv * d * pitch : nullptr;
+  const hipError_t e = launch_vt(v, dtype, v_tok, v_head, kv_len, hkv, d, vh, vl, pitch, 0, s);
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: V pack launch failed: %s", fn, hipGetErrorString(e));
+  return bsa_launch(fn, q, q_tok, q_head, k, k_tok, k_head, vh, vl, pitch, dtype, q_len, kv_len, hq, hkv, d, q_start,
+                    kv_start, block_mask, mask_hs, mask_rs, mask_off, block, causal, softmax_scale, out, out_dtype,
+                    lse, ws + packed_bytes(kv_len, hkv, d, dtype), s);
+}
+
+extern "C" xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok, int64_t q_head, const void* k,
+                                          int64_t k_tok, int64_t k_head, const void* packed_v, int64_t capacity,
+                                          int64_t v_token_offset, xa_dtype_t dtype, int64_t q_len, int64_t kv_len,
+                                          int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int64_t kv_start,
+                                          const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs,
+                                          int64_t mask_off, int32_t block, int32_t causal, float softmax_scale,
+                                          void* out, xa_dtype_t out_dtype, float* lse, void* workspace,
+                                          size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "bsa_prefill_packed";
+  xa_status_t st = validate_bsa_common(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, kv_len, hq, hkv, d,
+                                       q_start, kv_start, block_mask, mask_hs, mask_rs, mask_off, block,
+                                       softmax_scale, out, out_dtype, lse);
+  if (st != XA_OK) return st;
+  if (!packed_v || (uintptr_t)packed_v % 256 != 0) return fail(XA_EINVAL, "%s: packed_v must be 256-byte aligned", fn);
+  if (capacity <= 0 || v_token_offset < 0 || v_token_offset % 128 != 0)
+    return fail(XA_EINVAL, "%s: need capacity > 0 and v_token_offset a non-negative multiple of 128", fn);
+  const int64_t pitch = packed_pitch(capacity);
+  if (v_token_offset + (kv_len + 127) / 128 * 128 > pitch)
+    return fail(XA_EINVAL, "%s: packed tokens [%lld, %lld) exceed the capacity %lld", fn,
+                (long long)v_token_offset, (long long)(v_token_offset + kv_len), (long long)pitch);
+  const size_t need = bsa_prefill_packed_workspace_size(q_len, kv_len, hq, hkv, d, dtype);
+  if (need > 0 && (!workspace || ws_bytes < need || (uintptr_t)workspace % 256 != 0))
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                ws_bytes);
+  const bf16* vh = static_cast<const bf16*>(packed_v);
+  const bf16* vl = dtype == XA_F32 ? vh + (size_t)hkv * d * pitch : nullptr;
+  return bsa_launch(fn, q, q_tok, q_head, k, k_tok, k_head, vh + v_token_offset, vl ? vl + v_token_offset : nullptr,
+                    pitch, dtype, q_len, kv_len, hq, hkv, d, q_start, kv_start, block_mask, mask_hs, mask_rs,
+                    mask_off, block, causal, softmax_scale, out, out_dtype, lse, static_cast<char*>(workspace),
+                    reinterpret_cast<hipStream_t>(stream));
 }

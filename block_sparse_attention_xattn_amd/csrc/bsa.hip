@@ -353,13 +353,15 @@ __global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
 // Workspace preparation
 // ---------------------------------------------------------------------------
 
-// V [kv_len][hkv][D] (token-major, strided) -> Vt[hkv][D][pitch] in bf16
-// (hi and optionally lo planes), keys permuted by kSigma inside each group of
-// 16, zero beyond kv_len.  64x64 tiles through LDS for coalesced reads/writes.
+// V [n][hkv][D] (token-major, strided) -> packed V^T: per plane [hkv][D][pitch]
+// bf16 (hi plane, then the lo plane for fp32 input), tokens written at columns
+// token_offset .. token_offset + round_up(n, 128), keys permuted by kSigma
+// inside each group of 16, zero past n.  64x64 tiles through LDS for
+// coalesced reads and writes.
 template <typename T, bool SPLIT>
 __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, int64_t v_tok, int64_t v_head,
-                                                 int64_t kv_len, int D, bf16* vt_hi, bf16* vt_lo,
-                                                 int64_t pitch) {
+                                                 int64_t n_tok, int D, bf16* vt_hi, bf16* vt_lo,
+                                                 int64_t pitch, int64_t token_offset) {
   __shared__ float tile[64][65];
   const int64_t k0 = (int64_t)blockIdx.x * 64;
   const int d0 = blockIdx.y * 64;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, int64_
     const int kr = c / 8, dc = (c % 8) * 8;
     const int64_t key = k0 + kr;
     float vals[8];
-    if (key < kv_len) {
+    if (key < n_tok) {
       const T* src = v + key * v_tok + (int64_t)kvh * v_head + d0 + dc;
       if constexpr (sizeof(T) == 2) {
         const bf16x8 x = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, int64_
         hi[j] = (bf16)x;
       }
     }
-    const int64_t off = ((int64_t)kvh * D + d0 + dr) * pitch + k0 + pc;
+    const int64_t off = ((int64_t)kvh * D + d0 + dr) * pitch + token_offset + k0 + pc;
     *reinterpret_cast<u32x4*>(vt_hi + off) = as_u32x4(hi);
     if constexpr (SPLIT) *reinterpret_cast<u32x4*>(vt_lo + off) = as_u32x4(lo);
   }
@@ -460,15 +462,16 @@ template hipError_t launch_bsa<128, false, float>(const BsaParams&, hipStream_t)
 template hipError_t launch_bsa<128, true, bf16>(const BsaParams&, hipStream_t);
 template hipError_t launch_bsa<128, true, float>(const BsaParams&, hipStream_t);
 
-hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t kv_len, int hkv,
-                     int D, bf16* vt_hi, bf16* vt_lo, int64_t pitch, hipStream_t s) {
-  dim3 grid((unsigned)(pitch / 64), (unsigned)(D / 64), (unsigned)hkv);
+hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv,
+                     int D, bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s) {
+  const int64_t ext = (n_tok + 127) / 128 * 128;
+  dim3 grid((unsigned)(ext / 64), (unsigned)(D / 64), (unsigned)hkv);
   if (dt == XA_BF16)
-    hipLaunchKernelGGL((vt_kernel<bf16, false>), grid, dim3(256), 0, s, (const bf16*)v, v_tok, v_head, kv_len,
-                       D, vt_hi, vt_lo, pitch);
+    hipLaunchKernelGGL((vt_kernel<bf16, false>), grid, dim3(256), 0, s, (const bf16*)v, v_tok, v_head, n_tok,
+                       D, vt_hi, vt_lo, pitch, token_offset);
   else
-    hipLaunchKernelGGL((vt_kernel<float, true>), grid, dim3(256), 0, s, (const float*)v, v_tok, v_head, kv_len,
-                       D, vt_hi, vt_lo, pitch);
+    hipLaunchKernelGGL((vt_kernel<float, true>), grid, dim3(256), 0, s, (const float*)v, v_tok, v_head, n_tok,
+                       D, vt_hi, vt_lo, pitch, token_offset);
   return hipGetLastError();
 }
 

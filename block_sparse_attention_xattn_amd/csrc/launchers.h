@@ -53,8 +53,8 @@ struct SelParams {
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams& p, hipStream_t s);
-hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t kv_len, int hkv, int D,
-                     bf16* vt_hi, bf16* vt_lo, int64_t pitch, hipStream_t s);
+hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv, int D,
+                     bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s);
 hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,
                         hipStream_t s);
 template <int D, bool SPLIT>

@@ -11,8 +11,10 @@ The cache-block variant first reduces the history part of the mask to
 forced) and attends every 128-token block of the kept cache blocks, with
 dense causal attention inside the chunk.
 
-All buffers are allocated up front; a step only enqueues library calls on
-the current stream.
+V is kept packed once per layer in the attention kernel's layout: each chunk
+packs its own V rows when it starts (bsa_pack_v), and both attention calls
+read the packed buffer (bsa_prefill_packed).  All buffers are allocated up
+front; a step only enqueues library calls on the current stream.
 """
 from __future__ import annotations
 
@@ -61,9 +63,10 @@ class ChunkedPrefill:
         est_ws = max(B.xattn_estimate_workspace_size(min(chunk, self.L - p), p + min(chunk, self.L - p),
                                                      self.hq, self.hkv, self.d, stride, block, dt)
                      for p in self.starts)
-        bsa_ws = B.bsa_prefill_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
+        bsa_ws = B.bsa_prefill_packed_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
         self.est_ws = B.workspace(est_ws, dev)
-        self.bsa_ws = B.workspace(bsa_ws, dev)
+        self.bsa_ws = B.workspace(bsa_ws, dev) if bsa_ws > 0 else None
+        self.packed = B.PackedV(self.L, self.hkv, self.d, q.dtype, dev)
         self.out = torch.empty(self.L, self.hq, self.d, dtype=self.out_dtype, device=dev)
         self.bufs = []
         for p in self.starts:
@@ -88,7 +91,17 @@ class ChunkedPrefill:
                 lse=torch.empty(self.hq, c, dtype=torch.float32, device=dev),
                 **(kb or {})))
 
-    # -- the four calls of one chunk ------------------------------------------------
+    # -- the calls of one chunk --------------------------------------------------
+    def pack_history(self):
+        """Pack V rows before the first selected chunk (produced by earlier chunks)."""
+        p0 = self.starts[0]
+        if p0 > 0:
+            B.bsa_pack_v(self.v[:p0], self.packed, 0)
+
+    def pack(self, b: ChunkBuffers):
+        c = b.scores.shape[1] * self.block
+        B.bsa_pack_v(self.v[b.p:b.p + c], self.packed, b.p)
+
     def estimate(self, b: ChunkBuffers):
         c = b.scores.shape[1] * self.block
         B.xattn_estimate(self.q[b.p:b.p + c], self.k[:b.p + c], b.p, self.stride, self.threshold, self.block,
@@ -108,14 +121,15 @@ class ChunkedPrefill:
         qc = self.q[p:p + c]
         if p > 0:
             if b.keep_any_blocks is not None:
-                B.bsa_prefill(qc, self.k[:p], self.v[:p], p, 0, b.keep_any_blocks.view(1, 1, -1), 0, False,
-                              out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws, mask_head_stride=0, mask_row_stride=0)
+                B.bsa_prefill_packed(qc, self.k[:p], self.packed, 0, p, 0, b.keep_any_blocks.view(1, 1, -1), 0,
+                                     False, out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws, mask_head_stride=0,
+                                     mask_row_stride=0)
             else:
-                B.bsa_prefill(qc, self.k[:p], self.v[:p], p, 0, b.mask, 0, False,
-                              out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws)
+                B.bsa_prefill_packed(qc, self.k[:p], self.packed, 0, p, 0, b.mask, 0, False,
+                                     out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws)
         cur_mask = None if b.keep_any_blocks is not None else b.mask
-        B.bsa_prefill(qc, self.k[p:p + c], self.v[p:p + c], p, p, cur_mask, 0, True,
-                      out=b.o_cur, lse=b.l_cur if p > 0 else b.lse, ws=self.bsa_ws)
+        B.bsa_prefill_packed(qc, self.k[p:p + c], self.packed, p, p, p, cur_mask, 0, True,
+                             out=b.o_cur, lse=b.l_cur if p > 0 else b.lse, ws=self.bsa_ws)
 
     def merge(self, b: ChunkBuffers):
         if b.p == 0:
@@ -125,12 +139,14 @@ class ChunkedPrefill:
 
     def run_chunk(self, i: int):
         b = self.bufs[i]
+        self.pack(b)
         self.estimate(b)
         self.reduce(b)
         self.attend(b)
         self.merge(b)
 
     def run(self):
+        self.pack_history()
         for i in range(len(self.bufs)):
             self.run_chunk(i)
         return self.out

@@ -6,7 +6,8 @@
  *   1. xattn_estimate          -- stride-S antidiagonal importance estimate and
  *                                 cumulative-threshold block selection;
  *   2. bsa_prefill             -- block-sparse flash attention over the kept
- *                                 128-token blocks, returning out and LSE;
+ *      (bsa_pack_v,              128-token blocks, returning out and LSE
+ *       bsa_prefill_packed)      (variant reading V packed once per chunk);
  *   3. attn_merge              -- LSE merge of two partial attention results;
  *   4. xattn_mask_to_cache_blocks -- 128-token block mask -> cache blocks.
  *
@@ -124,8 +125,8 @@ xa_status_t xattn_estimate(const void* q, int64_t q_tok_stride, int64_t q_head_s
  *   partial); num_q_heads % num_kv_heads == 0.
  * Outputs: out  : out_dtype [q_len][num_q_heads][head_dim] (XA_F32 or XA_BF16)
  *          lse  : float [num_q_heads][q_len], natural log.
- * Workspace: at least bsa_prefill_workspace_size(...) bytes (holds V
- *   transposed per kv head, and for XA_F32 the bf16 hi/lo planes).
+ * Workspace: at least bsa_prefill_workspace_size(...) bytes (holds V packed as
+ *   described under bsa_pack_v, and for XA_F32 the bf16 hi/lo planes of Q and K).
  * ------------------------------------------------------------------------ */
 size_t bsa_prefill_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype);
@@ -141,6 +142,50 @@ xa_status_t bsa_prefill(const void* q, int64_t q_tok_stride, int64_t q_head_stri
                         int32_t block, int32_t causal, float softmax_scale,
                         void* out, xa_dtype_t out_dtype, float* lse,
                         void* workspace, size_t workspace_bytes, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Packed V for repeated attention calls over one growing key/value cache
+ *
+ * The attention kernel reads V transposed (per kv head: head_dim rows of
+ * tokens, keys permuted inside each group of 16 into the order the MFMA
+ * fragments use).  bsa_prefill builds that layout in its workspace on every
+ * call; for chunked prefill (XAttentionBSAPolicy.compute_chunked_prefill: each
+ * chunk attends the whole history, then its own keys) the caller can instead
+ * pack each chunk's V rows once, when they are produced, and call
+ * bsa_prefill_packed for every later chunk.
+ *
+ * bsa_packed_v_bytes: bytes of a packed buffer holding `capacity` tokens
+ *   (rounded up to 128) for num_kv_heads heads (two bf16 planes for XA_F32).
+ * bsa_pack_v: writes V rows 0 .. n_tokens-1 ([n_tokens][hkv][head_dim],
+ *   strided, dtype XA_BF16 or XA_F32) as packed tokens token_offset ..
+ *   token_offset+n_tokens-1; packed tokens up to the next multiple of 128 are
+ *   zeroed.  token_offset must be a multiple of 128 and the range must fit in
+ *   capacity.  packed_v must be 256-byte aligned device memory.
+ * bsa_prefill_packed: bsa_prefill with V taken from packed tokens
+ *   v_token_offset .. v_token_offset+kv_len-1 of packed_v (a multiple of 128;
+ *   same dtype as when packed).  Workspace: bsa_prefill_packed_workspace_size
+ *   bytes (0 for XA_BF16; workspace may then be NULL).
+ * ------------------------------------------------------------------------ */
+size_t bsa_packed_v_bytes(int64_t capacity, int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype);
+
+xa_status_t bsa_pack_v(const void* v, int64_t v_tok_stride, int64_t v_head_stride, xa_dtype_t dtype,
+                       int64_t n_tokens, int32_t num_kv_heads, int32_t head_dim, void* packed_v,
+                       int64_t capacity, int64_t token_offset, xa_stream_t stream);
+
+size_t bsa_prefill_packed_workspace_size(int64_t q_len, int64_t kv_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, xa_dtype_t dtype);
+
+xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                               const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                               const void* packed_v, int64_t capacity, int64_t v_token_offset,
+                               xa_dtype_t dtype, int64_t q_len, int64_t kv_len,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t q_start_pos, int64_t kv_start,
+                               const uint8_t* block_mask, int64_t mask_head_stride,
+                               int64_t mask_row_stride, int64_t mask_kb_offset,
+                               int32_t block, int32_t causal, float softmax_scale,
+                               void* out, xa_dtype_t out_dtype, float* lse,
+                               void* workspace, size_t workspace_bytes, xa_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)

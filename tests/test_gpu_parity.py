@@ -186,3 +186,30 @@ def test_small_multichunk_prefill_end_to_end():
     if same:
         PAR.check_out_lse(_np(out), np.concatenate([_np(b.lse) for b in run.bufs], axis=1), ref["out"], ref["lse"],
                           PAR.OUT_ATOL_BF16)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_packed_v_appends_and_offsets(dtype):
+    """V packed chunk by chunk, then attention over history and chunk from the packed buffer."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, L, C = 4, 2, 128, 1024, 384
+    q = _rand((L, hq, d), dtype, 70)
+    k = _rand((L, hkv, d), dtype, 71)
+    v = _rand((L, hkv, d), dtype, 72)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    packed = B.PackedV(L, hkv, d, dtype, DEV)
+    for p0 in range(0, L, C):                     # last piece is ragged (256 tokens)
+        B.bsa_pack_v(vd[p0:p0 + C], packed, p0)
+    p = 768
+    rng = np.random.default_rng(7)
+    mask = (rng.random((hq, (L - p) // 128, L // 128)) < 0.6).astype(np.uint8)
+    md = torch.from_numpy(mask).to(DEV)
+    tol = PAR.OUT_ATOL_BF16 if dtype == torch.bfloat16 else PAR.OUT_ATOL_F32
+    ro, rl = O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, mask, 0, False)
+    go, gl = B.bsa_prefill_packed(qd[p:], kd[:p], packed, 0, p, 0, md, 0, False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    PAR.check_out_lse(_np(go), _np(gl), ro, rl, tol)
+    ro, rl = O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True)
+    go, gl = B.bsa_prefill_packed(qd[p:], kd[p:], packed, p, p, p, md, 0, True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    PAR.check_out_lse(_np(go), _np(gl), ro, rl, tol)
