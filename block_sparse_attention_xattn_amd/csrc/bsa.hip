@@ -350,6 +350,230 @@ __global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel.
+//
+//   * workgroup = (query head, 128-row query block), 4 waves; wave w owns
+//     query rows 32w .. 32w+31 against all 128 keys of each kept block, so no
+//     cross-wave merge is needed;
+//   * two workgroups share a CU (<= 256 registers per wave, 68 KiB LDS each):
+//     their barriers are independent, so one workgroup's softmax (VALU) runs
+//     while the other's QK^T / PV (MFMA) run on the same SIMDs;
+//   * K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no
+//     staging registers): lane L of a wave-instruction lands at byte 16*L of a
+//     1 KiB run, so the 16-byte chunk a lane fetches is chosen such that LDS
+//     slot s of row r holds chunk s ^ (r mod 16) (XOR swizzle: fragment reads
+//     of 16 consecutive rows hit 16 distinct bank groups);
+//   * one K and one V buffer: the next K tile is fetched as soon as every
+//     wave has finished Q K^T, the next V tile as soon as P V is done, so each
+//     fetch overlaps the other half of the block's work;
+//   * the running max is only moved when a row's max grows by more than 2^8
+//     (P <= 256 in between), so the O rescale is rare.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag(const char* tile, int row, int chunk) {
+  constexpr int KCH = D / 8;
+  return *reinterpret_cast<const bf16x8*>(tile + row * (KCH * 16) + ((chunk ^ (row & (KCH - 1))) << 4));
+}
+
+__device__ __forceinline__ void g2lds16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaParams P) {
+  constexpr int KCH = D / 8;              // 16-byte chunks per K row
+  constexpr int KTB = 128 * KCH * 16;     // K tile bytes
+  constexpr int VTB = D * 256;            // V^T tile bytes (D rows x 128 keys)
+  constexpr int NKK = D / 16;
+  constexpr int NMD = D / 32;
+  constexpr int KI = KCH / 2;             // K load instructions per wave
+  constexpr int VI = D / 16;              // V load instructions per wave
+  constexpr float kRescale = 8.0f;        // log2 headroom before the running max moves
+  __shared__ __attribute__((aligned(1024))) char smem[KTB + VTB];
+  __shared__ int s_list[kListMax];
+  __shared__ int s_cnt;
+
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  int h, qb;
+  bsa_decode(blockIdx.x, P.group, P.hkv, P.n_qb, h, qb);
+  const int kvh = h / P.group;
+  const int64_t row = (int64_t)qb * kBlk + wave * 32 + n;
+  const int64_t q_glob = P.q_start + row;
+  const int64_t wave_q_lo = P.q_start + (int64_t)qb * kBlk + wave * 32;
+  const float c = P.scale_log2;
+
+  bf16x8 qf[NKK];
+  {
+    const int64_t off = row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q_hi + off + kk * 16));
+  }
+  f32x16 o[NMD];
+#pragma unroll
+  for (int i = 0; i < NMD; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;  // raw (unscaled) reference max of this lane's row
+  float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
+
+  const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
+  const int64_t gb0 = P.kv_start / kBlk;
+  int64_t jb_end = nkb;
+  if (P.causal) {
+    const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
+    jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
+  }
+  const uint8_t* mrow =
+      P.mask ? P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
+  const bf16* kg = P.k_hi + (int64_t)kvh * P.k_head;
+  const bf16* vg = P.vt_hi + (int64_t)kvh * P.vt_head;
+  char* kt = smem;
+  char* vt = smem + KTB;
+
+  auto issue_k = [&](int jb) {
+    const int64_t j0 = (int64_t)jb * kBlk;
+    const bf16* base = kg + j0 * P.k_tok;
+    const int rows_left = (int)((P.kv_len - j0) < kBlk ? (P.kv_len - j0) : kBlk);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int inst = wave * KI + i;
+      const int lin = inst * 64 + lane;
+      int r = lin / KCH;
+      const int ch = (lin % KCH) ^ (r & (KCH - 1));
+      r = r < rows_left ? r : rows_left - 1;  // rows past the tail are masked later
+      g2lds16(base + (int64_t)r * P.k_tok + ch * 8, kt + inst * 1024);
+    }
+  };
+  auto issue_v = [&](int jb) {
+    const bf16* base = vg + (int64_t)jb * kBlk;
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int inst = wave * VI + i;
+      const int lin = inst * 64 + lane;
+      const int r = lin >> 4;
+      const int ch = (lin & 15) ^ (r & 15);
+      g2lds16(base + (int64_t)r * P.vt_pitch + ch * 8, vt + inst * 1024);
+    }
+  };
+
+  for (int64_t seg = 0; seg < jb_end; seg += kListMax) {
+    const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
+    if (wave == 0) {
+      int cnt = 0;
+      for (int64_t base = seg; base < seg_end; base += 64) {
+        const int64_t jb = base + lane;
+        const bool keep = jb < seg_end && (mrow == nullptr || mrow[jb] != 0);
+        const uint64_t bal = __ballot(keep);
+        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1));
+        if (keep) s_list[pos] = (int)jb;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) s_cnt = cnt;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    if (cnt > 0) {
+      issue_k(s_list[0]);
+      issue_v(s_list[0]);
+    }
+    for (int it = 0; it < cnt; ++it) {
+      const int jb = s_list[it];
+      // K(it) landed (V(it) may still be in flight behind it)
+      __builtin_amdgcn_s_waitcnt(0x3f70 | VI);  // vmcnt(VI): only this wave's V loads may remain
+      __syncthreads();
+      f32x16 sacc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          sacc[mt] = mfma32(lds_frag<D>(kt, mt * 32 + n, 2 * kk + hh), qf[kk], sacc[mt]);
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): V(it) landed for this wave
+      __syncthreads();                     // K tile free, V tile complete
+      if (it + 1 < cnt) issue_k(s_list[it + 1]);
+
+      // mask keys past the tail / in the future of this lane's row
+      const int64_t key0 = (int64_t)jb * kBlk;
+      if ((key0 + kBlk > P.kv_len) || (P.causal && P.kv_start + key0 + kBlk - 1 > wave_q_lo)) {
+        int64_t lim = P.kv_len - 1 - key0;
+        if (P.causal && q_glob - P.kv_start - key0 < lim) lim = q_glob - P.kv_start - key0;
+        const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kl = mt * 32 + 8 * (i / 4) + (i % 4);
+            sacc[mt][i] = kl <= lim32 ? sacc[mt][i] : -INFINITY;
+          }
+      }
+      // online softmax with a lazily moved reference max
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool upd = mx > m_run && (m_run == -INFINITY || (mx - m_run) * c > kRescale);
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const float m_new = upd ? mx : m_run;
+        const float alpha = upd ? fast_exp2((m_run - m_new) * c) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) o[md] *= alpha;
+      }
+      const float mref = m_run == -INFINITY ? 0.f : m_run * c;
+      bf16x8 pf[8];
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[k2 >> 1][8 * (k2 & 1) + j], c, -mref));
+          l_run += p;
+          pf[k2][j] = (bf16)p;
+        }
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2)
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) o[md] = mfma32(lds_frag<128>(vt, md * 32 + n, 2 * k2 + hh), pf[k2], o[md]);
+      __syncthreads();  // V tile free
+      if (it + 1 < cnt) issue_v(s_list[it + 1]);
+    }
+    __syncthreads();  // s_list is rewritten by the next segment
+  }
+
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  float inv = 0.f, lse_v = -INFINITY;
+  if (l_row > 0.f) {
+    inv = 1.f / l_row;
+    lse_v = (m_run * c + log2f(l_row)) * kLn2;
+  }
+  OutT* out = reinterpret_cast<OutT*>(P.out);
+  const int64_t obase = row * ((int64_t)P.hq * D) + (int64_t)h * D;
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = md * 32 + 8 * g4 + 4 * hh;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[md][g4 * 4 + e] * inv;
+      if constexpr (sizeof(OutT) == 2) {
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (bf16)v[e];
+        *reinterpret_cast<u32x2*>(out + obase + d0) = __builtin_bit_cast(u32x2, pk);
+      } else {
+        *reinterpret_cast<f32x4*>(out + obase + d0) = f32x4{v[0], v[1], v[2], v[3]};
+      }
+    }
+  if (hh == 0) P.lse[(int64_t)h * P.q_len + row] = lse_v;
+}
+
+// ---------------------------------------------------------------------------
 // Workspace preparation
 // ---------------------------------------------------------------------------
 
@@ -449,7 +673,10 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams& p, hipStream_t s) {
   const int grid = p.hq * p.n_qb;
-  hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(grid), dim3(kThreads), 0, s, p);
+  if constexpr (!SPLIT && D == 128)
+    hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
