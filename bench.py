@@ -200,6 +200,20 @@ def main():
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
 
+    # per launch kind (history vs in-chunk), averaged over the timed steps
+    kinds = []
+    for b in run.bufs:
+        if b.p > 0:
+            kinds.append("history")
+        kinds.append("in_chunk")
+    by_kind = {}
+    for i, kind in enumerate(kinds):
+        durs = bsa_durs[i::n_launch]
+        f, t = by_kind.get(kind, (0.0, 0.0))
+        by_kind[kind] = (f + launches[i] * len(durs), t + sum(durs))
+    bsa_by_kind = {k2: {"ms_per_step": round(t / a.steps, 3), "tflops": round(f / (t * 1e-3) / 1e12, 1)}
+                   for k2, (f, t) in by_kind.items()}
+
     out = {
         "metric": "sparse prefill tokens/s per layer (estimate+BSA) at 32K/128K; % bf16 MFMA peak",
         "value": round(value, 1),
@@ -225,6 +239,7 @@ def main():
         "effective_frac_of_peak": round(eff_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "density": round(dens, 4),
         "parts_ms": {k2: round(v2, 3) for k2, v2 in parts.items()},
+        "bsa_by_kind": bsa_by_kind,
         "estimate_gflop": round(est_flops / 1e9, 1),
         "bsa_gflop": round(bsa_flops_step / 1e9, 1),
     }

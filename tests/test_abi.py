@@ -1,0 +1,144 @@
+"""The C ABI on the host (no GPU needed): exports, size queries, argument errors.
+
+Every call here fails validation (or is a pure size query), so nothing is
+launched; the library only has to load.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_xattn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xattn.h")
+FAKE = ctypes.c_void_p(0x100000)      # 256-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(0x200000)
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail(f"{B.LIB_PATH} not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"xattn_estimate", "bsa_prefill", "attn_merge", "xattn_mask_to_cache_blocks", "bsa_pack_v",
+            "bsa_prefill_packed"} <= set(names)
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in xattn.h but not exported"
+
+
+def test_version_and_sizes(lib):
+    assert lib.xattn_version().startswith(b"xattn-gfx950")
+    # estimate workspace: Hq * nKB * (q_len / stride) fp32 log-sum-exp partials (bf16 input)
+    assert B.xattn_estimate_workspace_size(4096, 32768, 32, 8, 128, 8, 128, B.XA_BF16) == 32 * 256 * 512 * 4
+    assert B.xattn_estimate_workspace_size(4096, 32768, 32, 8, 128, 8, 128, B.XA_F32) > 32 * 256 * 512 * 4
+    # packed V: hkv * d * round_up(capacity, 128) bf16, two planes for fp32
+    assert B.bsa_packed_v_bytes(1000, 8, 128, B.XA_BF16) == 8 * 128 * 1024 * 2
+    assert B.bsa_packed_v_bytes(1000, 8, 128, B.XA_F32) == 2 * 8 * 128 * 1024 * 2
+    assert B.bsa_prefill_packed_workspace_size(4096, 32768, 32, 8, 128, B.XA_BF16) == 0
+    assert B.bsa_prefill_workspace_size(4096, 32768, 32, 8, 128, B.XA_BF16) == 8 * 128 * 32768 * 2
+
+
+def _estimate(lib, **over):
+    a = dict(q=FAKE, qt=32 * 128, qh=128, k=FAKE2, kt=8 * 128, kh=128, dt=B.XA_BF16, ql=4096, kl=8192, hq=32,
+             hkv=8, d=128, p=4096, S=8, blk=128, tau=0.9, sc=FAKE, m=FAKE2, ws=FAKE, wsb=1 << 40, st=None)
+    a.update(over)
+    return lib.xattn_estimate(a["q"], a["qt"], a["qh"], a["k"], a["kt"], a["kh"], a["dt"], a["ql"], a["kl"], a["hq"],
+                              a["hkv"], a["d"], a["p"], a["S"], a["blk"], a["tau"], a["sc"], a["m"], a["ws"],
+                              a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=96), B.XA_EUNSUPPORTED),
+    (dict(S=3), B.XA_EUNSUPPORTED),
+    (dict(blk=64), B.XA_EUNSUPPORTED),
+    (dict(hq=30), B.XA_EINVAL),
+    (dict(ql=4000), B.XA_EINVAL),
+    (dict(p=100), B.XA_EINVAL),
+    (dict(kl=8000), B.XA_EINVAL),
+    (dict(q=None), B.XA_EINVAL),
+    (dict(qt=33), B.XA_EINVAL),
+    (dict(tau=-0.5), B.XA_EINVAL),
+    (dict(sc=None), B.XA_EINVAL),
+    (dict(wsb=16), B.XA_EWORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), B.XA_EWORKSPACE),
+    (dict(dt=7), B.XA_EUNSUPPORTED),
+])
+def test_estimate_rejects(lib, over, status):
+    assert _estimate(lib, **over) == status
+    assert lib.xattn_last_error()
+
+
+def _bsa_packed(lib, **over):
+    a = dict(q=FAKE, qt=32 * 128, qh=128, k=FAKE2, kt=8 * 128, kh=128, pv=FAKE, cap=8192, voff=0, dt=B.XA_BF16,
+             ql=4096, kl=4096, hq=32, hkv=8, d=128, p=4096, ks=0, m=None, mhs=0, mrs=0, moff=0, blk=128, causal=0,
+             scale=0.0, out=FAKE2, odt=B.XA_BF16, lse=FAKE, ws=None, wsb=0, st=None)
+    a.update(over)
+    return lib.bsa_prefill_packed(a["q"], a["qt"], a["qh"], a["k"], a["kt"], a["kh"], a["pv"], a["cap"], a["voff"],
+                                  a["dt"], a["ql"], a["kl"], a["hq"], a["hkv"], a["d"], a["p"], a["ks"], a["m"],
+                                  a["mhs"], a["mrs"], a["moff"], a["blk"], a["causal"], a["scale"], a["out"],
+                                  a["odt"], a["lse"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=256), B.XA_EUNSUPPORTED),
+    (dict(blk=256), B.XA_EUNSUPPORTED),
+    (dict(hkv=5), B.XA_EINVAL),
+    (dict(ql=100), B.XA_EINVAL),
+    (dict(kl=0), B.XA_EINVAL),
+    (dict(ks=64), B.XA_EINVAL),
+    (dict(voff=64), B.XA_EINVAL),
+    (dict(voff=4096, kl=8192), B.XA_EINVAL),        # past the packed capacity
+    (dict(m=FAKE, moff=40), B.XA_EINVAL),           # mask offset past the first key block
+    (dict(m=FAKE, mhs=-1), B.XA_EINVAL),
+    (dict(out=None), B.XA_EINVAL),
+    (dict(out=ctypes.c_void_p(0x100008)), B.XA_EINVAL),
+    (dict(scale=-1.0), B.XA_EINVAL),
+    (dict(odt=3), B.XA_EUNSUPPORTED),
+    (dict(pv=ctypes.c_void_p(0x100010)), B.XA_EINVAL),
+    (dict(dt=B.XA_F32, ws=None, wsb=0), B.XA_EWORKSPACE),   # fp32 needs split-plane workspace
+])
+def test_bsa_packed_rejects(lib, over, status):
+    assert _bsa_packed(lib, **over) == status
+
+
+def test_merge_and_reducer_reject(lib):
+    P = ctypes.c_void_p
+    assert lib.attn_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B.XA_BF16, 128, 4, 100, None) == B.XA_EINVAL
+    assert lib.attn_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 9, 128, 4, 128, None) == B.XA_EUNSUPPORTED
+    assert lib.attn_merge(None, FAKE, FAKE, FAKE, FAKE, FAKE, B.XA_BF16, 128, 4, 128, None) == B.XA_EINVAL
+    assert lib.attn_merge(FAKE, FAKE, FAKE, FAKE, P(0x100004), FAKE, B.XA_BF16, 128, 4, 128, None) == B.XA_EINVAL
+    assert lib.attn_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B.XA_BF16, 0, 4, 128, None) == B.XA_OK  # empty
+    assert lib.xattn_mask_to_cache_blocks(FAKE, 0, 4, 64, 0, 0, 0, 8, 8, 1, FAKE, FAKE, FAKE, None) == B.XA_EINVAL
+    assert lib.xattn_mask_to_cache_blocks(FAKE, 4, 4, 64, 0, 0, 0, 9, 8, 1, FAKE, FAKE, FAKE, None) == B.XA_EINVAL
+    assert lib.xattn_mask_to_cache_blocks(None, 4, 4, 64, 0, 0, 0, 8, 8, 1, FAKE, FAKE, FAKE, None) == B.XA_EINVAL
+    assert lib.xattn_mask_to_cache_blocks(FAKE, 4, 4, 64, 0, 0, 0, 0, 8, 1, FAKE, FAKE, FAKE, None) == B.XA_OK
+
+
+def test_pack_v_rejects(lib):
+    assert lib.bsa_pack_v(FAKE, 1024, 128, B.XA_BF16, 256, 8, 128, FAKE2, 100, 0, None) == B.XA_EINVAL  # capacity
+    assert lib.bsa_pack_v(FAKE, 1024, 128, B.XA_BF16, 256, 8, 128, FAKE2, 1024, 64, None) == B.XA_EINVAL  # offset
+    assert lib.bsa_pack_v(FAKE, 1024, 128, B.XA_BF16, 256, 8, 96, FAKE2, 1024, 0, None) == B.XA_EUNSUPPORTED
+    assert lib.bsa_pack_v(FAKE, 1024, 128, B.XA_BF16, 256, 8, 128, ctypes.c_void_p(0x200010), 1024, 0,
+                          None) == B.XA_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
