@@ -44,28 +44,38 @@ def count_flops(run):
     attention: 4*d*128^2 flop per computed (head, query block, key block) tile
     (QK^T and PV), diagonal tiles counted whole; estimate: 2*(d*S) flop per
     visible (reshaped row, reshaped column) pair.
-    Returns (bsa_flops_per_launch list in launch order, estimate_flops, density).
+    Returns (attention flops per launch in launch order, estimate flops,
+    density, attention flops split {history, in_chunk}).
     """
     import numpy as np
     d, S, blk = run.d, run.stride, run.block
     per_tile = 4.0 * d * blk * blk
+    fused = run.q.dtype.is_floating_point and run.q.element_size() == 2 and d == 128
     launches = []
+    split = {"history": 0.0, "in_chunk": 0.0}
     est = 0.0
     sel = tot = 0
     for b in run.bufs:
         m = b.mask.cpu().numpy().astype(bool)
         hq, nqb, nkb = m.shape
         cur = b.p // blk
+        parts = []
         if b.p > 0:
             if b.keep_any_blocks is not None:
                 kept = int(b.keep_any_blocks.cpu().numpy().astype(bool).sum())
-                launches.append(per_tile * kept * hq * nqb)
+                parts.append(("history", per_tile * kept * hq * nqb))
             else:
-                launches.append(per_tile * float(m[:, :, :cur].sum()))
+                parts.append(("history", per_tile * float(m[:, :, :cur].sum())))
         if b.keep_any_blocks is not None:
-            launches.append(per_tile * hq * nqb * (nqb + 1) / 2)
+            parts.append(("in_chunk", per_tile * hq * nqb * (nqb + 1) / 2))
         else:
-            launches.append(per_tile * float(m[:, :, cur:].sum()))
+            parts.append(("in_chunk", per_tile * float(m[:, :, cur:].sum())))
+        for kind, f in parts:
+            split[kind] += f
+        if fused:
+            launches.append(sum(f for _, f in parts))
+        else:
+            launches.extend(f for _, f in parts)
         causal = np.arange(nkb)[None, :] <= (cur + np.arange(nqb))[:, None]
         sel += int((m & causal[None]).sum())
         tot += int(causal.sum()) * hq
@@ -73,7 +83,7 @@ def count_flops(run):
         cdiag = b.p // S
         vis = float(np.sum(cdiag + np.arange(R) + 1))
         est += 2.0 * d * S * vis * hq
-    return launches, est, sel / max(tot, 1)
+    return launches, est, sel / max(tot, 1), split
 
 
 def cpu_baseline(name, groups):
@@ -150,17 +160,21 @@ def main():
 
     from block_sparse_attention_xattn_amd import binding as B
     orig_bsa = B.bsa_prefill_packed
+    orig_seg = B.bsa_prefill_segments
 
-    def bsa_timed(*args, **kw):
-        mark("bsa_launch:start")
-        r = orig_bsa(*args, **kw)
-        mark("bsa_launch:end")
-        return r
+    def wrap(fn):
+        def inner(*args, **kw):
+            mark("bsa_launch:start")
+            r = fn(*args, **kw)
+            mark("bsa_launch:end")
+            return r
+        return inner
 
     run.estimate = timed("estimate", orig_est)
     run.merge = timed("merge", orig_merge)
     run.pack = timed("pack", orig_pack)
-    B.bsa_prefill_packed = bsa_timed
+    B.bsa_prefill_packed = wrap(orig_bsa)
+    B.bsa_prefill_segments = wrap(orig_seg)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -172,6 +186,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     B.bsa_prefill_packed = orig_bsa
+    B.bsa_prefill_segments = orig_seg
     gpu_ms = e0.elapsed_time(e1)
     step_ms = max(gpu_ms, wall * 1e3) / a.steps
 
@@ -190,7 +205,7 @@ def main():
     for kk in parts:
         parts[kk] /= a.steps
 
-    launches, est_flops, dens = count_flops(run)
+    launches, est_flops, dens, split = count_flops(run)
     bsa_flops_step = sum(launches)
     n_launch = len(launches)
     assert len(bsa_durs) == n_launch * a.steps, (len(bsa_durs), n_launch)
@@ -199,20 +214,6 @@ def main():
     eff_tflops = (bsa_flops_step + est_flops) / (step_ms * 1e-3) / 1e12
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
-
-    # per launch kind (history vs in-chunk), averaged over the timed steps
-    kinds = []
-    for b in run.bufs:
-        if b.p > 0:
-            kinds.append("history")
-        kinds.append("in_chunk")
-    by_kind = {}
-    for i, kind in enumerate(kinds):
-        durs = bsa_durs[i::n_launch]
-        f, t = by_kind.get(kind, (0.0, 0.0))
-        by_kind[kind] = (f + launches[i] * len(durs), t + sum(durs))
-    bsa_by_kind = {k2: {"ms_per_step": round(t / a.steps, 3), "tflops": round(f / (t * 1e-3) / 1e12, 1)}
-                   for k2, (f, t) in by_kind.items()}
 
     out = {
         "metric": "sparse prefill tokens/s per layer (estimate+BSA) at 32K/128K; % bf16 MFMA peak",
@@ -239,7 +240,7 @@ def main():
         "effective_frac_of_peak": round(eff_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "density": round(dens, 4),
         "parts_ms": {k2: round(v2, 3) for k2, v2 in parts.items()},
-        "bsa_by_kind": bsa_by_kind,
+        "bsa_gflop_split": {k2: round(v2 / 1e9, 1) for k2, v2 in split.items()},
         "estimate_gflop": round(est_flops / 1e9, 1),
         "bsa_gflop": round(bsa_flops_step / 1e9, 1),
     }

@@ -26,6 +26,15 @@ STATUS_NAMES = {0: "XA_OK", 1: "XA_EINVAL", 2: "XA_EUNSUPPORTED", 3: "XA_EWORKSP
 _lib = None
 
 
+class Segment(ctypes.Structure):
+    """xa_segment_t (xattn.h)."""
+    _fields_ = [("k", ctypes.c_void_p), ("k_tok_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("kv_len", ctypes.c_int64), ("kv_start", ctypes.c_int64), ("v_token_offset", ctypes.c_int64),
+                ("block_mask", ctypes.c_void_p), ("mask_head_stride", ctypes.c_int64),
+                ("mask_row_stride", ctypes.c_int64), ("mask_kb_offset", ctypes.c_int64), ("causal", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
 class XattnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -57,6 +66,9 @@ def _declare(lib):
     lib.bsa_prefill_packed.restype = ctypes.c_int
     lib.bsa_prefill_packed.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
                                        I64, I64, P, I64, I64, I64, I32, I32, F, P, ctypes.c_int, P, P, SZ, P]
+    lib.bsa_prefill_segments.restype = ctypes.c_int
+    lib.bsa_prefill_segments.argtypes = [P, I64, I64, P, I64, ctypes.c_int, I64, I32, I32, I32, I64,
+                                         ctypes.POINTER(Segment), I32, I32, F, ctypes.c_int, P, SZ, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -239,6 +251,35 @@ def bsa_prefill_packed(q, k, packed: PackedV, v_token_offset: int, q_start_pos: 
                                     1 if causal else 0, float(softmax_scale), _ptr(out), odt, _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
+
+
+def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax_scale: float = 0.0, block: int = 128,
+                         stream=None):
+    """Several attention problems over one query chunk in one launch (see xattn.h).
+
+    segments: list of dicts with keys k, kv_start, v_token_offset, block_mask (or None), causal, out, lse and
+    optionally mask_kb_offset, mask_head_stride, mask_row_stride.  Returns [(out, lse), ...].
+    """
+    _qkv_check(q, "q")
+    dt = _dtype_code(q)
+    q_len, hq, d = q.shape
+    arr = (Segment * len(segments))()
+    keep = []
+    for i, g in enumerate(segments):
+        k = g["k"]
+        _qkv_check(k, "k")
+        m = g.get("block_mask")
+        hs = g.get("mask_head_stride", m.stride(0) if m is not None else 0)
+        rs = g.get("mask_row_stride", m.stride(1) if m is not None else 0)
+        arr[i] = Segment(k.data_ptr(), k.stride(0), k.stride(1), k.shape[0], g["kv_start"], g["v_token_offset"],
+                         None if m is None else m.data_ptr(), hs, rs, g.get("mask_kb_offset", 0),
+                         1 if g["causal"] else 0, g["out"].data_ptr(), g["lse"].data_ptr())
+        keep.append((g["out"], g["lse"]))
+    odt = _dtype_code(segments[0]["out"])
+    _check(lib().bsa_prefill_segments(_ptr(q), q.stride(0), q.stride(1), _ptr(packed.buf), packed.capacity, dt,
+                                      q_len, hq, packed.hkv, d, q_start_pos, arr, len(segments), block,
+                                      float(softmax_scale), odt, None, 0, _stream(stream)))
+    return keep
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -247,15 +247,26 @@ xa_status_t validate_bsa_common(const char* fn, const void* q, int64_t q_tok, in
   return XA_OK;
 }
 
-// Launch the attention kernel once the packed V (hi/lo planes) is in place.
-xa_status_t bsa_launch(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
-                       int64_t k_head, const bf16* vt_hi, const bf16* vt_lo, int64_t pitch, xa_dtype_t dtype,
-                       int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, int64_t q_start,
-                       int64_t kv_start, const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs,
-                       int64_t mask_off, int32_t block, int32_t causal, float softmax_scale, void* out,
-                       xa_dtype_t out_dtype, float* lse, char* split_ws, hipStream_t s) {
+// Fill the kernel parameters of one attention problem (V already packed).
+BsaParams bsa_params(const bf16* q, int64_t q_tok, int64_t q_head, const bf16* q_lo, const bf16* k, int64_t k_tok,
+                     int64_t k_head, const bf16* k_lo, const bf16* vt_hi, const bf16* vt_lo, int64_t pitch,
+                     int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, int64_t q_start,
+                     int64_t kv_start, const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs, int64_t mask_off,
+                     int32_t block, int32_t causal, float softmax_scale, void* out, float* lse) {
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   BsaParams p{};
+  p.q_hi = q;
+  p.q_lo = q_lo;
+  p.q_tok = q_tok;
+  p.q_head = q_head;
+  p.k_hi = k;
+  p.k_lo = k_lo;
+  p.k_tok = k_tok;
+  p.k_head = k_head;
+  p.vt_hi = vt_hi;
+  p.vt_lo = vt_lo;
+  p.vt_pitch = pitch;
+  p.vt_head = (int64_t)d * pitch;
   p.q_len = q_len;
   p.kv_len = kv_len;
   p.hq = hq;
@@ -272,48 +283,68 @@ xa_status_t bsa_launch(const char* fn, const void* q, int64_t q_tok, int64_t q_h
   p.scale_log2 = scale * kLog2e;
   p.out = out;
   p.lse = lse;
-  p.vt_pitch = pitch;
-  p.vt_head = (int64_t)d * pitch;
-  p.vt_hi = vt_hi;
-  p.vt_lo = vt_lo;
+  return p;
+}
+
+// Split fp32 Q and K into bf16 hi/lo planes in split_ws (fp32 inputs only).
+xa_status_t split_qk(const char* fn, const void* q, int64_t& q_tok, int64_t& q_head, const void* k, int64_t& k_tok,
+                     int64_t& k_head, int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                     char* split_ws, const bf16** qh, const bf16** ql, const bf16** kh, const bf16** kl,
+                     hipStream_t s) {
+  const size_t pq = align256((size_t)q_len * hq * d * 2);
+  const size_t pk = align256((size_t)kv_len * hkv * d * 2);
+  bf16* qh_ = reinterpret_cast<bf16*>(split_ws);
+  bf16* ql_ = reinterpret_cast<bf16*>(split_ws + pq);
+  bf16* kh_ = reinterpret_cast<bf16*>(split_ws + 2 * pq);
+  bf16* kl_ = reinterpret_cast<bf16*>(split_ws + 2 * pq + pk);
   hipError_t e;
-  if (dtype == XA_BF16) {
-    p.q_hi = static_cast<const bf16*>(q);
-    p.k_hi = static_cast<const bf16*>(k);
-    p.q_tok = q_tok;
-    p.q_head = q_head;
-    p.k_tok = k_tok;
-    p.k_head = k_head;
-  } else {
-    const size_t pq = align256((size_t)q_len * hq * d * 2);
-    const size_t pk = align256((size_t)kv_len * hkv * d * 2);
-    bf16* qh = reinterpret_cast<bf16*>(split_ws);
-    bf16* ql = reinterpret_cast<bf16*>(split_ws + pq);
-    bf16* kh = reinterpret_cast<bf16*>(split_ws + 2 * pq);
-    bf16* kl = reinterpret_cast<bf16*>(split_ws + 2 * pq + pk);
-    if ((e = launch_split((const float*)q, q_tok, q_head, q_len, hq, d, qh, ql, s)) != hipSuccess ||
-        (e = launch_split((const float*)k, k_tok, k_head, kv_len, hkv, d, kh, kl, s)) != hipSuccess)
-      return fail(XA_EHIP, "%s: split launch failed: %s", fn, hipGetErrorString(e));
-    p.q_hi = qh;
-    p.q_lo = ql;
-    p.k_hi = kh;
-    p.k_lo = kl;
-    p.q_tok = (int64_t)hq * d;
-    p.q_head = d;
-    p.k_tok = (int64_t)hkv * d;
-    p.k_head = d;
-  }
+  if ((e = launch_split((const float*)q, q_tok, q_head, q_len, hq, d, qh_, ql_, s)) != hipSuccess ||
+      (e = launch_split((const float*)k, k_tok, k_head, kv_len, hkv, d, kh_, kl_, s)) != hipSuccess)
+    return fail(XA_EHIP, "%s: split launch failed: %s", fn, hipGetErrorString(e));
+  *qh = qh_;
+  *ql = ql_;
+  *kh = kh_;
+  *kl = kl_;
+  q_tok = (int64_t)hq * d;
+  q_head = d;
+  k_tok = (int64_t)hkv * d;
+  k_head = d;
+  return XA_OK;
+}
+
+xa_status_t run_bsa(const char* fn, const BsaParams* segs, int n, int32_t d, xa_dtype_t dtype, xa_dtype_t out_dtype,
+                    hipStream_t s) {
   const bool split = dtype == XA_F32;
   const bool obf = out_dtype == XA_BF16;
+  hipError_t e;
   if (d == 128) {
-    if (split) e = obf ? launch_bsa<128, true, bf16>(p, s) : launch_bsa<128, true, float>(p, s);
-    else e = obf ? launch_bsa<128, false, bf16>(p, s) : launch_bsa<128, false, float>(p, s);
+    if (split) e = obf ? launch_bsa<128, true, bf16>(segs, n, s) : launch_bsa<128, true, float>(segs, n, s);
+    else e = obf ? launch_bsa<128, false, bf16>(segs, n, s) : launch_bsa<128, false, float>(segs, n, s);
   } else {
-    if (split) e = obf ? launch_bsa<64, true, bf16>(p, s) : launch_bsa<64, true, float>(p, s);
-    else e = obf ? launch_bsa<64, false, bf16>(p, s) : launch_bsa<64, false, float>(p, s);
+    if (split) e = obf ? launch_bsa<64, true, bf16>(segs, n, s) : launch_bsa<64, true, float>(segs, n, s);
+    else e = obf ? launch_bsa<64, false, bf16>(segs, n, s) : launch_bsa<64, false, float>(segs, n, s);
   }
   if (e != hipSuccess) return fail(XA_EHIP, "%s: attention launch failed: %s", fn, hipGetErrorString(e));
   return XA_OK;
+}
+
+// Launch the attention kernel once the packed V (hi/lo planes) is in place.
+xa_status_t bsa_launch(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                       int64_t k_head, const bf16* vt_hi, const bf16* vt_lo, int64_t pitch, xa_dtype_t dtype,
+                       int64_t q_len, int64_t kv_len, int32_t hq, int32_t hkv, int32_t d, int64_t q_start,
+                       int64_t kv_start, const uint8_t* block_mask, int64_t mask_hs, int64_t mask_rs,
+                       int64_t mask_off, int32_t block, int32_t causal, float softmax_scale, void* out,
+                       xa_dtype_t out_dtype, float* lse, char* split_ws, hipStream_t s) {
+  const bf16 *qh = static_cast<const bf16*>(q), *ql = nullptr, *kh = static_cast<const bf16*>(k), *kl = nullptr;
+  if (dtype == XA_F32) {
+    const xa_status_t st = split_qk(fn, q, q_tok, q_head, k, k_tok, k_head, q_len, kv_len, hq, hkv, d, split_ws, &qh,
+                                    &ql, &kh, &kl, s);
+    if (st != XA_OK) return st;
+  }
+  const BsaParams p = bsa_params(qh, q_tok, q_head, ql, kh, k_tok, k_head, kl, vt_hi, vt_lo, pitch, q_len, kv_len,
+                                 hq, hkv, d, q_start, kv_start, block_mask, mask_hs, mask_rs, mask_off, block, causal,
+                                 softmax_scale, out, lse);
+  return run_bsa(fn, &p, 1, d, dtype, out_dtype, s);
 }
 }  // namespace
 
@@ -418,4 +449,42 @@ extern "C" xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok, int64_t 
                     pitch, dtype, q_len, kv_len, hq, hkv, d, q_start, kv_start, block_mask, mask_hs, mask_rs,
                     mask_off, block, causal, softmax_scale, out, out_dtype, lse, static_cast<char*>(workspace),
                     reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_t q_head, const void* packed_v,
+                                            int64_t capacity, xa_dtype_t dtype, int64_t q_len, int32_t hq,
+                                            int32_t hkv, int32_t d, int64_t q_start, const xa_segment_t* segments,
+                                            int32_t n_segments, int32_t block, float softmax_scale,
+                                            xa_dtype_t out_dtype, void* workspace, size_t ws_bytes,
+                                            xa_stream_t stream) {
+  const char* fn = "bsa_prefill_segments";
+  if (!segments || n_segments < 1 || n_segments > kMaxSegments)
+    return fail(XA_EINVAL, "%s: need 1..%d segments (got %d)", fn, kMaxSegments, n_segments);
+  if (dtype == XA_F32) return fail(XA_EUNSUPPORTED, "%s: segmented calls take XA_BF16 inputs", fn);
+  if (!packed_v || (uintptr_t)packed_v % 256 != 0) return fail(XA_EINVAL, "%s: packed_v must be 256-byte aligned", fn);
+  const int64_t pitch = packed_pitch(capacity);
+  for (int i = 0; i < n_segments; ++i) {
+    const xa_segment_t& g = segments[i];
+    xa_status_t st = validate_bsa_common(fn, q, q_tok, q_head, g.k, g.k_tok_stride, g.k_head_stride, dtype, q_len,
+                                         g.kv_len, hq, hkv, d, q_start, g.kv_start, g.block_mask, g.mask_head_stride,
+                                         g.mask_row_stride, g.mask_kb_offset, block, softmax_scale, g.out, out_dtype,
+                                         g.lse);
+    if (st != XA_OK) return st;
+    if (capacity <= 0 || g.v_token_offset < 0 || g.v_token_offset % 128 != 0 ||
+        g.v_token_offset + (g.kv_len + 127) / 128 * 128 > pitch)
+      return fail(XA_EINVAL, "%s: segment %d: packed tokens [%lld, %lld) outside the capacity %lld", fn, i,
+                  (long long)g.v_token_offset, (long long)(g.v_token_offset + g.kv_len), (long long)pitch);
+  }
+  (void)workspace;
+  (void)ws_bytes;
+  BsaParams segs[kMaxSegments];
+  const bf16* vh = static_cast<const bf16*>(packed_v);
+  for (int i = 0; i < n_segments; ++i) {
+    const xa_segment_t& g = segments[i];
+    segs[i] = bsa_params(static_cast<const bf16*>(q), q_tok, q_head, nullptr, static_cast<const bf16*>(g.k),
+                         g.k_tok_stride, g.k_head_stride, nullptr, vh + g.v_token_offset, nullptr, pitch, q_len,
+                         g.kv_len, hq, hkv, d, q_start, g.kv_start, g.block_mask, g.mask_head_stride,
+                         g.mask_row_stride, g.mask_kb_offset, block, g.causal, softmax_scale, g.out, g.lse);
+  }
+  return run_bsa(fn, segs, n_segments, d, dtype, out_dtype, reinterpret_cast<hipStream_t>(stream));
 }

@@ -380,7 +380,11 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds) {
 }
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaParams P) {
+__global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
+  int sidx = 0;
+  while (sidx + 1 < M.n_seg && (int)blockIdx.x >= M.wg_end[sidx]) ++sidx;
+  const BsaParams& P = M.seg[sidx];
+  const int bid = (int)blockIdx.x - (sidx ? M.wg_end[sidx - 1] : 0);
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
   constexpr int KTB = 128 * KCH * 16;     // K tile bytes
   constexpr int VTB = D * 256;            // V^T tile bytes (D rows x 128 keys)
@@ -392,6 +396,7 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaParams P) {
   __shared__ __attribute__((aligned(1024))) char smem[KTB + VTB];
   __shared__ int s_list[kListMax];
   __shared__ int s_cnt;
+  __shared__ int s_wcnt[4];
 
   const int wave = wave_id();
   const int lane = lane_id();
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaParams P) {
   const int hh = lane >> 5;
 
   int h, qb;
-  bsa_decode(blockIdx.x, P.group, P.hkv, P.n_qb, h, qb);
+  bsa_decode(bid, P.group, P.hkv, P.n_qb, h, qb);
   const int kvh = h / P.group;
   const int64_t row = (int64_t)qb * kBlk + wave * 32 + n;
   const int64_t q_glob = P.q_start + row;
@@ -460,17 +465,28 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaParams P) {
 
   for (int64_t seg = 0; seg < jb_end; seg += kListMax) {
     const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
-    if (wave == 0) {
-      int cnt = 0;
-      for (int64_t base = seg; base < seg_end; base += 64) {
+    {
+      // each wave scans a quarter of the segment: count, exchange, write
+      const int64_t quarter = ((seg_end - seg + 3) / 4 + 63) / 64 * 64;
+      const int64_t w0 = seg + wave * quarter;
+      const int64_t w1 = w0 + quarter < seg_end ? w0 + quarter : seg_end;
+      int mine = 0;
+      for (int64_t base = w0; base < w1; base += 64) {
         const int64_t jb = base + lane;
-        const bool keep = jb < seg_end && (mrow == nullptr || mrow[jb] != 0);
-        const uint64_t bal = __ballot(keep);
-        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1));
-        if (keep) s_list[pos] = (int)jb;
-        cnt += __popcll(bal);
+        mine += __popcll(__ballot(jb < w1 && (mrow == nullptr || mrow[jb] != 0)));
       }
-      if (lane == 0) s_cnt = cnt;
+      if (lane == 0) s_wcnt[wave] = mine;
+      __syncthreads();
+      int pos0 = 0;
+      for (int w = 0; w < wave; ++w) pos0 += s_wcnt[w];
+      for (int64_t base = w0; base < w1; base += 64) {
+        const int64_t jb = base + lane;
+        const bool keep = jb < w1 && (mrow == nullptr || mrow[jb] != 0);
+        const uint64_t bal = __ballot(keep);
+        if (keep) s_list[pos0 + __popcll(bal & ((1ull << lane) - 1))] = (int)jb;
+        pos0 += __popcll(bal);
+      }
+      if (wave == 3 && lane == 0) s_cnt = pos0;
     }
     __syncthreads();
     const int cnt = s_cnt;
@@ -671,23 +687,33 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
 
 // Explicit instantiation helpers used by the ABI layer.
 template <int D, bool SPLIT, typename OutT>
-hipError_t launch_bsa(const BsaParams& p, hipStream_t s) {
-  const int grid = p.hq * p.n_qb;
-  if constexpr (!SPLIT && D == 128)
-    hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(grid), dim3(kThreads), 0, s, p);
+hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s) {
+  if constexpr (!SPLIT && D == 128) {
+    BsaMulti m{};
+    int total = 0;
+    for (int i = 0; i < n_seg; ++i) {
+      m.seg[i] = segs[i];
+      total += segs[i].hq * segs[i].n_qb;
+      m.wg_end[i] = total;
+    }
+    m.n_seg = n_seg;
+    if (total > 0) hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+  } else {
+    for (int i = 0; i < n_seg; ++i)
+      hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(segs[i].hq * segs[i].n_qb), dim3(kThreads), 0, s,
+                         segs[i]);
+  }
   return hipGetLastError();
 }
 
-template hipError_t launch_bsa<64, false, bf16>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<64, false, float>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<64, true, bf16>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<64, true, float>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<128, false, bf16>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<128, false, float>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<128, true, bf16>(const BsaParams&, hipStream_t);
-template hipError_t launch_bsa<128, true, float>(const BsaParams&, hipStream_t);
+template hipError_t launch_bsa<64, false, bf16>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<64, false, float>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<64, true, bf16>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<64, true, float>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<128, false, bf16>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<128, false, float>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<128, true, bf16>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<128, true, float>(const BsaParams*, int, hipStream_t);
 
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv,
                      int D, bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s) {

@@ -51,8 +51,17 @@ struct SelParams {
   uint8_t* mask;  // [hq][n_qb][nkb]
 };
 
+// Up to kMaxSegments attention problems sharing Q, heads and packed V, run as
+// one grid (segment i owns workgroups wg_end[i-1] .. wg_end[i]-1).
+constexpr int kMaxSegments = 4;
+struct BsaMulti {
+  BsaParams seg[kMaxSegments];
+  int wg_end[kMaxSegments];
+  int n_seg;
+};
+
 template <int D, bool SPLIT, typename OutT>
-hipError_t launch_bsa(const BsaParams& p, hipStream_t s);
+hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s);
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv, int D,
                      bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s);
 hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,

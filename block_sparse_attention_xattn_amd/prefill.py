@@ -116,20 +116,29 @@ class ChunkedPrefill:
                                      keep_any_blocks=b.keep_any_blocks)
 
     def attend(self, b: ChunkBuffers):
+        """History (no causal rule) and the chunk's own keys (causal) in one segmented launch."""
         p = b.p
         c = b.scores.shape[1] * self.block
         qc = self.q[p:p + c]
+        segs = []
         if p > 0:
             if b.keep_any_blocks is not None:
-                B.bsa_prefill_packed(qc, self.k[:p], self.packed, 0, p, 0, b.keep_any_blocks.view(1, 1, -1), 0,
-                                     False, out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws, mask_head_stride=0,
-                                     mask_row_stride=0)
+                segs.append(dict(k=self.k[:p], kv_start=0, v_token_offset=0, block_mask=b.keep_any_blocks.view(1, 1, -1),
+                                 mask_head_stride=0, mask_row_stride=0, causal=False, out=b.o_hist, lse=b.l_hist))
             else:
-                B.bsa_prefill_packed(qc, self.k[:p], self.packed, 0, p, 0, b.mask, 0, False,
-                                     out=b.o_hist, lse=b.l_hist, ws=self.bsa_ws)
+                segs.append(dict(k=self.k[:p], kv_start=0, v_token_offset=0, block_mask=b.mask, causal=False,
+                                 out=b.o_hist, lse=b.l_hist))
         cur_mask = None if b.keep_any_blocks is not None else b.mask
-        B.bsa_prefill_packed(qc, self.k[p:p + c], self.packed, p, p, p, cur_mask, 0, True,
-                             out=b.o_cur, lse=b.l_cur if p > 0 else b.lse, ws=self.bsa_ws)
+        segs.append(dict(k=self.k[p:p + c], kv_start=p, v_token_offset=p, block_mask=cur_mask, causal=True,
+                         out=b.o_cur, lse=b.l_cur if p > 0 else b.lse))
+        if self.q.dtype == torch.bfloat16 and self.d == 128:
+            B.bsa_prefill_segments(qc, self.packed, p, segs)
+        else:
+            for g in segs:
+                B.bsa_prefill_packed(qc, g["k"], self.packed, g["v_token_offset"], p, g["kv_start"], g["block_mask"],
+                                     0, g["causal"], out=g["out"], lse=g["lse"], ws=self.bsa_ws,
+                                     mask_head_stride=g.get("mask_head_stride"),
+                                     mask_row_stride=g.get("mask_row_stride"))
 
     def merge(self, b: ChunkBuffers):
         if b.p == 0:

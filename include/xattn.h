@@ -188,6 +188,39 @@ xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok_stride, int64_t q_he
                                void* workspace, size_t workspace_bytes, xa_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Several attention problems over one query chunk in a single launch
+ *
+ * XAttentionBSAPolicy.compute_chunked_prefill attends a chunk twice -- the
+ * history without the causal rule and the chunk's own keys with it -- and
+ * merges the two partials.  bsa_prefill_segments runs up to 4 such segments
+ * (each exactly a bsa_prefill_packed call with its own keys, packed-V range,
+ * mask, causal flag and outputs, sharing Q, heads and the packed-V buffer) as
+ * one grid, segments in the order given (put the heaviest first).
+ * segments: HOST array of n_segments (1..4) descriptors.  XA_BF16 inputs only.
+ * workspace: unused (may be NULL).  Validation of every segment precedes the
+ * launch; errors as for bsa_prefill_packed.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const void* k;               /* [kv_len][num_kv_heads][head_dim] key rows of this segment */
+  int64_t k_tok_stride, k_head_stride;
+  int64_t kv_len, kv_start;    /* key row j is global position kv_start + j */
+  int64_t v_token_offset;      /* packed-V tokens v_token_offset .. +kv_len hold V of these rows */
+  const uint8_t* block_mask;   /* as for bsa_prefill; NULL = every block */
+  int64_t mask_head_stride, mask_row_stride, mask_kb_offset;
+  int32_t causal;
+  void* out;                   /* out_dtype [q_len][num_q_heads][head_dim] */
+  float* lse;                  /* [num_q_heads][q_len] */
+} xa_segment_t;
+
+xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                 const void* packed_v, int64_t capacity, xa_dtype_t dtype,
+                                 int64_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int64_t q_start_pos,
+                                 const xa_segment_t* segments, int32_t n_segments,
+                                 int32_t block, float softmax_scale, xa_dtype_t out_dtype,
+                                 void* workspace, size_t workspace_bytes, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)
  *
  * nano-vllm CLAUDE.md, "Online Softmax Merge - Triton Fused Kernel":

@@ -213,3 +213,34 @@ def test_packed_v_appends_and_offsets(dtype):
     go, gl = B.bsa_prefill_packed(qd[p:], kd[p:], packed, p, p, p, md, 0, True, out_dtype=torch.float32)
     torch.cuda.synchronize()
     PAR.check_out_lse(_np(go), _np(gl), ro, rl, tol)
+
+
+def test_segments_in_one_launch():
+    """History (non-causal, mask offset), the chunk's own keys (causal) and a broadcast-mask segment in one grid."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, L, p = 8, 2, 128, 1280, 768
+    q = _rand((L, hq, d), torch.bfloat16, 80)
+    k = _rand((L, hkv, d), torch.bfloat16, 81)
+    v = _rand((L, hkv, d), torch.bfloat16, 82)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
+    B.bsa_pack_v(vd, packed, 0)
+    rng = np.random.default_rng(9)
+    nqb, nkb = (L - p) // 128, L // 128
+    mask = (rng.random((hq, nqb, nkb)) < 0.5).astype(np.uint8)
+    row = (rng.random(p // 128) < 0.5).astype(np.uint8)
+    md, rowd = torch.from_numpy(mask).to(DEV), torch.from_numpy(row).to(DEV).view(1, 1, -1)
+    outs = [(torch.empty(L - p, hq, d, dtype=torch.float32, device=DEV),
+             torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(3)]
+    segs = [dict(k=kd[128:p], kv_start=128, v_token_offset=128, block_mask=md, causal=False,
+                 out=outs[0][0], lse=outs[0][1]),
+            dict(k=kd[p:], kv_start=p, v_token_offset=p, block_mask=md, causal=True, out=outs[1][0], lse=outs[1][1]),
+            dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=rowd, mask_head_stride=0, mask_row_stride=0,
+                 causal=False, out=outs[2][0], lse=outs[2][1])]
+    B.bsa_prefill_segments(qd[p:], packed, p, segs)
+    torch.cuda.synchronize()
+    refs = [O.bsa(_np(q[p:]), _np(k[128:p]), _np(v[128:p]), p, 128, mask, 0, False),
+            O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True),
+            O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, np.broadcast_to(row, (hq, nqb, p // 128)), 0, False)]
+    for (go, gl), (ro, rl) in zip(outs, refs):
+        PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
