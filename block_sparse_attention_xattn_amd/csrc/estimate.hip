@@ -156,6 +156,143 @@ __global__ __launch_bounds__(kEThreads) void est_gemm_kernel(EstParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16, head_dim 128: 256x256 output tile per 16-wave workgroup (4x4 waves of
+// 64x64), so every 16-byte fragment read from LDS feeds two MFMAs and each
+// byte fetched from L2 feeds twice the MFMA work of a 128x128 tile.  The
+// contraction is walked in slices of 64 head-dim columns of one stride step t
+// (query tokens r*S+S-1-t, key tokens c*S+t); slices go global -> LDS with
+// global_load_lds_dwordx4 into two alternating 64 KiB buffers (128-byte rows,
+// 16-byte chunk s of row r stored at slot s ^ ((r >> 1) & 7)), one barrier per
+// slice.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void est_g2lds16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+template <int HALF>
+__global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
+  constexpr int TILE = 256;
+  constexpr int SLICE_B = TILE * 128;      // one operand slice: 256 rows x 64 bf16
+  constexpr int BUF_B = 2 * SLICE_B;       // Q slice + K slice
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_B];
+
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int wr = wave & 3;
+  const int wc = wave >> 2;
+
+  const int n_rt = (P.R + TILE - 1) / TILE;
+  const int n_ct = (P.N + TILE - 1) / TILE;
+  const int total = P.hkv * n_ct * n_rt * P.group;
+  int w = xcd_remap(blockIdx.x, total);
+  const int j = w % P.group;
+  w /= P.group;
+  const int rt = w % n_rt;
+  w /= n_rt;
+  const int ct = w % n_ct;
+  const int kvh = w / n_ct;
+  const int h = kvh * P.group + j;
+
+  const int64_t cdiag = P.q_start / P.S;
+  const int r_hi = min(P.R - 1, rt * TILE + TILE - 1);
+  if ((int64_t)ct * TILE > cdiag + r_hi) return;
+
+  const int w_r0 = rt * TILE + wr * 64;
+  const int w_c0 = ct * TILE + wc * 64;
+  const bool wave_live = w_r0 < P.R && w_c0 < P.N && (int64_t)w_c0 <= cdiag + min(P.R - 1, w_r0 + 63);
+
+  // this lane's two load chunks per operand per slice (instructions 2*wave, 2*wave+1)
+  const bf16* qb = P.q_hi + (int64_t)h * P.q_head;
+  const bf16* kb = P.k_hi + (int64_t)kvh * P.k_head;
+  auto issue = [&](int slice, int buf) {
+    const int t = slice >> 1;
+    const int dof = (slice & 1) * 64;
+    char* dq = smem + buf * BUF_B;
+    char* dk = dq + SLICE_B;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int inst = wave * 2 + i;
+      const int lin = inst * 64 + lane;
+      const int r = lin >> 3;
+      const int ch = (lin & 7) ^ ((r >> 1) & 7);
+      int qr = rt * TILE + r;
+      qr = qr < P.R ? qr : P.R - 1;
+      int kc = ct * TILE + r;
+      kc = kc < P.N ? kc : P.N - 1;
+      const int64_t qtok = (int64_t)qr * P.S + (P.S - 1 - t);
+      const int64_t ktok = (int64_t)kc * P.S + t;
+      est_g2lds16(qb + qtok * P.q_tok + dof + ch * 8, dq + inst * 1024);
+      est_g2lds16(kb + ktok * P.k_tok + dof + ch * 8, dk + inst * 1024);
+    }
+  };
+  auto frag = [&](const char* base, int r, int ch) {
+    return *reinterpret_cast<const bf16x8*>(base + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+
+  const int n_slices = 2 * P.S;
+  issue(0, 0);
+  for (int sl = 0; sl < n_slices; ++sl) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // this wave's loads of slice sl have landed
+    __syncthreads();                     // ... and every wave's; buffer (sl+1)&1 is free
+    if (sl + 1 < n_slices) issue(sl + 1, (sl + 1) & 1);
+    if (wave_live) {
+      const char* qs = smem + (sl & 1) * BUF_B;
+      const char* ks = qs + SLICE_B;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) af[mt] = frag(ks, wc * 64 + mt * 32 + n, 2 * kk + hh);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) bfr[nt] = frag(qs, wr * 64 + nt * 32 + n, 2 * kk + hh);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(af[mt], bfr[nt], acc[mt][nt]);
+      }
+    }
+  }
+  if (!wave_live) return;
+
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = w_r0 + nt * 32 + n;
+    float x[32];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+        const bool ok = c < P.N && c <= cdiag + r;
+        x[mt * 16 + i] = ok ? acc[mt][nt][i] * P.scale_log2 : -INFINITY;
+      }
+#pragma unroll
+    for (int g0 = 0; g0 < 32; g0 += HALF) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = g0; v < g0 + HALF; ++v) mx = fmaxf(mx, x[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float s = 0.f;
+      const float ref = mx == -INFINITY ? 0.f : mx;
+#pragma unroll
+      for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(x[v] - ref);
+      s += __shfl_xor(s, 32);
+      const int kbk = w_c0 / (2 * HALF) + g0 / HALF;
+      if (hh == 0 && r < P.R && kbk < P.nkb)
+        P.lse_part[((int64_t)h * P.nkb + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Block sums + cumulative-threshold selection, one workgroup per
 // (head, query block).
 // ---------------------------------------------------------------------------
@@ -239,14 +376,15 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
     if (kb == diag) s_ad = a;
   }
   for (int kb = P.nkb + tid; kb < npow; kb += 256) keys[kb] = ~0ull;
-  part[tid] = tsum;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int k = 0; k < 256; ++k) t += part[k];
-    s_total = t;
+  {
+    double t = tsum;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+    if ((tid & 63) == 0) part[tid >> 6] = t;
+    __syncthreads();
+    if (tid == 0) s_total = part[0] + part[1] + part[2] + part[3];
+    __syncthreads();
   }
-  __syncthreads();
 
   const int n_other = nvis - 2 > 0 ? nvis - 2 : 0;  // sortable blocks (0 and diag excluded)
   if (!all && n_other > 0) {
@@ -273,20 +411,21 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
     const int p1 = min(n_other, p0 + seg);
     double loc = 0.0;
     for (int p = p0; p < p1; ++p) loc += (double)__uint_as_float(0xffffffffu - (unsigned)(keys[p] >> 32));
-    part[tid] = loc;
-    __syncthreads();
-    if (tid == 0) {
-      double run = 0.0;
-      for (int k = 0; k < 256; ++k) {
-        const double v = part[k];
-        part[k] = run;
-        run += v;
-      }
+    // exclusive scan of the 256 segment sums: inclusive scan inside each wave, then wave offsets
+    const int lane = tid & 63;
+    double incl = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double up = __shfl_up(incl, o);
+      if (lane >= o) incl += up;
     }
+    if (lane == 63) part[tid >> 6] = incl;
     __syncthreads();
+    double wave_off = 0.0;
+    for (int w = 0; w < (tid >> 6); ++w) wave_off += part[w];
     const double forced_mass = (double)s_a0 + (diag > 0 ? (double)s_ad : 0.0);
     const double need = (double)P.threshold * s_total;
-    double run = forced_mass + part[tid];
+    double run = forced_mass + wave_off + (incl - loc);
     for (int p = p0; p < p1; ++p) {
       const unsigned long long key = keys[p];
       if (run < need) mrow[(unsigned)(key & 0xffffffffu)] = 1;
@@ -302,6 +441,18 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
 
 template <int D, bool SPLIT>
 hipError_t launch_est_gemm(const EstParams& p, hipStream_t s) {
+  if constexpr (D == 128 && !SPLIT) {
+    const int n_rt = (p.R + 255) / 256, n_ct = (p.N + 255) / 256;
+    const int grid = p.hkv * n_ct * n_rt * p.group;
+    switch (p.b) {
+      case 8: hipLaunchKernelGGL((est_gemm2_kernel<4>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 16: hipLaunchKernelGGL((est_gemm2_kernel<8>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 32: hipLaunchKernelGGL((est_gemm2_kernel<16>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((est_gemm2_kernel<32>), dim3(grid), dim3(1024), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int grid = p.hkv * p.n_ct * p.n_rt * p.group;
   switch (p.b) {
     case 8: hipLaunchKernelGGL((est_gemm_kernel<D, SPLIT, 4>), dim3(grid), dim3(kEThreads), 0, s, p); break;
