@@ -69,6 +69,8 @@ def _declare(lib):
     lib.bsa_prefill_segments.restype = ctypes.c_int
     lib.bsa_prefill_segments.argtypes = [P, I64, I64, P, I64, ctypes.c_int, I64, I32, I32, I32, I64,
                                          ctypes.POINTER(Segment), I32, I32, F, ctypes.c_int, P, SZ, P]
+    lib.bsa_prefill_segments_workspace_size.restype = SZ
+    lib.bsa_prefill_segments_workspace_size.argtypes = [I64, I32, I32]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -253,12 +255,17 @@ def bsa_prefill_packed(q, k, packed: PackedV, v_token_offset: int, q_start_pos: 
     return out, lse
 
 
+def bsa_prefill_segments_workspace_size(q_len: int, num_q_heads: int, n_segments: int) -> int:
+    return int(lib().bsa_prefill_segments_workspace_size(q_len, num_q_heads, n_segments))
+
+
 def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax_scale: float = 0.0, block: int = 128,
-                         stream=None):
+                         ws=None, stream=None):
     """Several attention problems over one query chunk in one launch (see xattn.h).
 
     segments: list of dicts with keys k, kv_start, v_token_offset, block_mask (or None), causal, out, lse and
-    optionally mask_kb_offset, mask_head_stride, mask_row_stride.  Returns [(out, lse), ...].
+    optionally mask_kb_offset, mask_head_stride, mask_row_stride.  ws: the work-order buffer
+    (bsa_prefill_segments_workspace_size bytes; allocated here when None).  Returns [(out, lse), ...].
     """
     _qkv_check(q, "q")
     dt = _dtype_code(q)
@@ -276,9 +283,11 @@ def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax
                          1 if g["causal"] else 0, g["out"].data_ptr(), g["lse"].data_ptr())
         keep.append((g["out"], g["lse"]))
     odt = _dtype_code(segments[0]["out"])
+    if ws is None:
+        ws = workspace(bsa_prefill_segments_workspace_size(q_len, hq, len(segments)), q.device)
     _check(lib().bsa_prefill_segments(_ptr(q), q.stride(0), q.stride(1), _ptr(packed.buf), packed.capacity, dt,
                                       q_len, hq, packed.hkv, d, q_start_pos, arr, len(segments), block,
-                                      float(softmax_scale), odt, None, 0, _stream(stream)))
+                                      float(softmax_scale), odt, _ptr(ws), ws.numel(), _stream(stream)))
     return keep
 
 

@@ -313,16 +313,16 @@ xa_status_t split_qk(const char* fn, const void* q, int64_t& q_tok, int64_t& q_h
 }
 
 xa_status_t run_bsa(const char* fn, const BsaParams* segs, int n, int32_t d, xa_dtype_t dtype, xa_dtype_t out_dtype,
-                    hipStream_t s) {
+                    hipStream_t s, const BsaPlan* plan = nullptr) {
   const bool split = dtype == XA_F32;
   const bool obf = out_dtype == XA_BF16;
   hipError_t e;
   if (d == 128) {
-    if (split) e = obf ? launch_bsa<128, true, bf16>(segs, n, s) : launch_bsa<128, true, float>(segs, n, s);
-    else e = obf ? launch_bsa<128, false, bf16>(segs, n, s) : launch_bsa<128, false, float>(segs, n, s);
+    if (split) e = obf ? launch_bsa<128, true, bf16>(segs, n, plan, s) : launch_bsa<128, true, float>(segs, n, plan, s);
+    else e = obf ? launch_bsa<128, false, bf16>(segs, n, plan, s) : launch_bsa<128, false, float>(segs, n, plan, s);
   } else {
-    if (split) e = obf ? launch_bsa<64, true, bf16>(segs, n, s) : launch_bsa<64, true, float>(segs, n, s);
-    else e = obf ? launch_bsa<64, false, bf16>(segs, n, s) : launch_bsa<64, false, float>(segs, n, s);
+    if (split) e = obf ? launch_bsa<64, true, bf16>(segs, n, plan, s) : launch_bsa<64, true, float>(segs, n, plan, s);
+    else e = obf ? launch_bsa<64, false, bf16>(segs, n, plan, s) : launch_bsa<64, false, float>(segs, n, plan, s);
   }
   if (e != hipSuccess) return fail(XA_EHIP, "%s: attention launch failed: %s", fn, hipGetErrorString(e));
   return XA_OK;
@@ -451,6 +451,13 @@ extern "C" xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok, int64_t 
                     reinterpret_cast<hipStream_t>(stream));
 }
 
+extern "C" size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t n_segments) {
+  if (q_len <= 0 || num_q_heads <= 0 || n_segments < 1 || n_segments > kMaxSegments) return 0;
+  const int64_t n_items = (int64_t)n_segments * num_q_heads * ((q_len + 127) / 128);
+  if (n_items > (int64_t)1 << 30) return 0;
+  return bsa_plan_bytes(n_items);
+}
+
 extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_t q_head, const void* packed_v,
                                             int64_t capacity, xa_dtype_t dtype, int64_t q_len, int32_t hq,
                                             int32_t hkv, int32_t d, int64_t q_start, const xa_segment_t* segments,
@@ -475,8 +482,15 @@ extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_
       return fail(XA_EINVAL, "%s: segment %d: packed tokens [%lld, %lld) outside the capacity %lld", fn, i,
                   (long long)g.v_token_offset, (long long)(g.v_token_offset + g.kv_len), (long long)pitch);
   }
-  (void)workspace;
-  (void)ws_bytes;
+  const size_t need = bsa_prefill_segments_workspace_size(q_len, hq, n_segments);
+  if (need == 0) return fail(XA_EINVAL, "%s: too many work items (q_len %lld, %d heads)", fn, (long long)q_len, hq);
+  if (!workspace || (uintptr_t)workspace % 256 != 0 || ws_bytes < need)
+    return fail(XA_EWORKSPACE, "%s: needs a 256-byte aligned workspace of %zu bytes (got %zu at %p)", fn, need,
+                ws_bytes, workspace);
+  char* w = static_cast<char*>(workspace);
+  const int64_t n_items = (int64_t)n_segments * hq * ((q_len + 127) / 128);
+  const size_t arr = ((size_t)n_items * 4 + 255) / 256 * 256;
+  const BsaPlan plan{reinterpret_cast<int*>(w + 256), reinterpret_cast<int*>(w + 256 + arr), reinterpret_cast<int*>(w)};
   BsaParams segs[kMaxSegments];
   const bf16* vh = static_cast<const bf16*>(packed_v);
   for (int i = 0; i < n_segments; ++i) {
@@ -486,5 +500,5 @@ extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_
                          g.kv_len, hq, hkv, d, q_start, g.kv_start, g.block_mask, g.mask_head_stride,
                          g.mask_row_stride, g.mask_kb_offset, block, g.causal, softmax_scale, g.out, g.lse);
   }
-  return run_bsa(fn, segs, n_segments, d, dtype, out_dtype, reinterpret_cast<hipStream_t>(stream));
+  return run_bsa(fn, segs, n_segments, d, dtype, out_dtype, reinterpret_cast<hipStream_t>(stream), &plan);
 }

@@ -381,10 +381,17 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds) {
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
+  __shared__ int s_item;
+  int item = (int)blockIdx.x;
+  if (M.order) {
+    if (threadIdx.x == 0) s_item = M.order[atomicAdd(M.ticket, 1)];
+    __syncthreads();
+    item = s_item;
+  }
   int sidx = 0;
-  while (sidx + 1 < M.n_seg && (int)blockIdx.x >= M.wg_end[sidx]) ++sidx;
+  while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
   const BsaParams& P = M.seg[sidx];
-  const int bid = (int)blockIdx.x - (sidx ? M.wg_end[sidx - 1] : 0);
+  const int bid = item - (sidx ? M.wg_end[sidx - 1] : 0);
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
   constexpr int KTB = 128 * KCH * 16;     // K tile bytes
   constexpr int VTB = D * 256;            // V^T tile bytes (D rows x 128 keys)
@@ -685,9 +692,88 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Longest-first ordering of a segmented launch.  The kept-tile count of a
+// work item's row varies several-fold across heads and query blocks; taking
+// items in dispatch order leaves long rows for the end of the grid.  Two small
+// kernels count each item's kept tiles and sort the item ids by descending
+// count (counting sort in one workgroup); the attention workgroups then take
+// items in that order as they start (greedy longest-processing-time list
+// scheduling).  Ordering changes only which workgroup computes an item.
+constexpr int kPlanBins = 4096;  // counts >= kPlanBins-1 share the last bin
+
+// One wave per work item: kept key blocks before the causal limit.
+__global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items, int* __restrict__ weights) {
+  const int item = (int)blockIdx.x * 4 + wave_id();
+  const int lane = lane_id();
+  if (item >= n_items) return;
+  int sidx = 0;
+  while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
+  const BsaParams& P = M.seg[sidx];
+  const int bid = item - (sidx ? M.wg_end[sidx - 1] : 0);
+  int h, qb;
+  bsa_decode(bid, P.group, P.hkv, P.n_qb, h, qb);
+  const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
+  int64_t jb_end = nkb;
+  if (P.causal) {
+    const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
+    jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
+  }
+  int cnt;
+  if (P.mask == nullptr) {
+    cnt = jb_end < kPlanBins ? (int)jb_end : kPlanBins;
+  } else {
+    const uint8_t* mrow = P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (P.kv_start / kBlk - P.mask_off);
+    cnt = 0;
+    for (int64_t jb = lane; jb < jb_end; jb += 64) cnt += mrow[jb] != 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  }
+  if (lane == 0) weights[item] = cnt;
+}
+
+// One workgroup: order[] = item ids by descending weight; ticket = 0.
+__global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int* __restrict__ weights,
+                                                         int* __restrict__ order, int* __restrict__ ticket) {
+  __shared__ int bins[kPlanBins];
+  __shared__ int wsum[16];
+  const int t = (int)threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t >> 6;
+  for (int b = t; b < kPlanBins; b += 1024) bins[b] = 0;
+  __syncthreads();
+  for (int i = t; i < n_items; i += 1024) atomicAdd(&bins[min(weights[i], kPlanBins - 1)], 1);
+  __syncthreads();
+  // exclusive scan from the highest bin down: thread t owns bins top-4t .. top-4t-3
+  int v[4], own = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = bins[kPlanBins - 1 - 4 * t - j];
+    own += v[j];
+  }
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - own;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bins[kPlanBins - 1 - 4 * t - j] = run;
+    run += v[j];
+  }
+  __syncthreads();
+  for (int i = t; i < n_items; i += 1024) order[atomicAdd(&bins[min(weights[i], kPlanBins - 1)], 1)] = i;
+  if (t == 0) *ticket = 0;
+}
+
 // Explicit instantiation helpers used by the ABI layer.
 template <int D, bool SPLIT, typename OutT>
-hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s) {
+hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s) {
   if constexpr (!SPLIT && D == 128) {
     BsaMulti m{};
     int total = 0;
@@ -697,7 +783,16 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s) {
       m.wg_end[i] = total;
     }
     m.n_seg = n_seg;
-    if (total > 0) hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+    if (total > 0) {
+      if (plan) {
+        hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights);
+        hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
+                           plan->order, plan->ticket);
+        m.order = plan->order;
+        m.ticket = plan->ticket;
+      }
+      hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+    }
   } else {
     for (int i = 0; i < n_seg; ++i)
       hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(segs[i].hq * segs[i].n_qb), dim3(kThreads), 0, s,
@@ -706,14 +801,14 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template hipError_t launch_bsa<64, false, bf16>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<64, false, float>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<64, true, bf16>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<64, true, float>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<128, false, bf16>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<128, false, float>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<128, true, bf16>(const BsaParams*, int, hipStream_t);
-template hipError_t launch_bsa<128, true, float>(const BsaParams*, int, hipStream_t);
+template hipError_t launch_bsa<64, false, bf16>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<64, false, float>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<64, true, bf16>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<64, true, float>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<128, false, bf16>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<128, false, float>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<128, true, bf16>(const BsaParams*, int, const BsaPlan*, hipStream_t);
+template hipError_t launch_bsa<128, true, float>(const BsaParams*, int, const BsaPlan*, hipStream_t);
 
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv,
                      int D, bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s) {

@@ -52,16 +52,33 @@ struct SelParams {
 };
 
 // Up to kMaxSegments attention problems sharing Q, heads and packed V, run as
-// one grid (segment i owns workgroups wg_end[i-1] .. wg_end[i]-1).
+// one grid.  Work item i (one (head, query block) of one segment) belongs to
+// segment s when wg_end[s-1] <= i < wg_end[s].  Without an order, workgroup b
+// runs item b; with one, each workgroup takes the next ticket t as it starts
+// and runs item order[t].
 constexpr int kMaxSegments = 4;
 struct BsaMulti {
   BsaParams seg[kMaxSegments];
   int wg_end[kMaxSegments];
   int n_seg;
+  const int* order;  // item ids, longest kept-tile list first (or null)
+  int* ticket;       // start counter, zeroed by the ordering kernel
 };
 
+// Device buffers for the longest-first ordering of a segmented launch.
+struct BsaPlan {
+  int* weights;  // [n_items] kept tiles per item
+  int* order;    // [n_items]
+  int* ticket;
+};
+// Bytes of the ordering buffers for n_items work items (ticket, weights, order).
+inline size_t bsa_plan_bytes(int64_t n_items) {
+  const size_t a = ((size_t)n_items * 4 + 255) / 256 * 256;
+  return 256 + 2 * a;
+}
+
 template <int D, bool SPLIT, typename OutT>
-hipError_t launch_bsa(const BsaParams* segs, int n_seg, hipStream_t s);
+hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s);
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv, int D,
                      bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s);
 hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,

@@ -13,7 +13,8 @@ dense causal attention inside the chunk.
 
 V is kept packed once per layer in the attention kernel's layout: each chunk
 packs its own V rows when it starts (bsa_pack_v), and both attention calls
-read the packed buffer (bsa_prefill_packed).  All buffers are allocated up
+read the packed buffer (one bsa_prefill_segments launch for bf16, head_dim
+128; two bsa_prefill_packed calls otherwise).  All buffers are allocated up
 front; a step only enqueues library calls on the current stream.
 """
 from __future__ import annotations
@@ -66,6 +67,7 @@ class ChunkedPrefill:
         bsa_ws = B.bsa_prefill_packed_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
         self.est_ws = B.workspace(est_ws, dev)
         self.bsa_ws = B.workspace(bsa_ws, dev) if bsa_ws > 0 else None
+        self.seg_ws = B.workspace(B.bsa_prefill_segments_workspace_size(chunk, self.hq, 2), dev)
         self.packed = B.PackedV(self.L, self.hkv, self.d, q.dtype, dev)
         self.out = torch.empty(self.L, self.hq, self.d, dtype=self.out_dtype, device=dev)
         self.bufs = []
@@ -132,7 +134,7 @@ class ChunkedPrefill:
         segs.append(dict(k=self.k[p:p + c], kv_start=p, v_token_offset=p, block_mask=cur_mask, causal=True,
                          out=b.o_cur, lse=b.l_cur if p > 0 else b.lse))
         if self.q.dtype == torch.bfloat16 and self.d == 128:
-            B.bsa_prefill_segments(qc, self.packed, p, segs)
+            B.bsa_prefill_segments(qc, self.packed, p, segs, ws=self.seg_ws)
         else:
             for g in segs:
                 B.bsa_prefill_packed(qc, g["k"], self.packed, g["v_token_offset"], p, g["kv_start"], g["block_mask"],

@@ -195,10 +195,21 @@ xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok_stride, int64_t q_he
  * merges the two partials.  bsa_prefill_segments runs up to 4 such segments
  * (each exactly a bsa_prefill_packed call with its own keys, packed-V range,
  * mask, causal flag and outputs, sharing Q, heads and the packed-V buffer) as
- * one grid, segments in the order given (put the heaviest first).
- * segments: HOST array of n_segments (1..4) descriptors.  XA_BF16 inputs only.
- * workspace: unused (may be NULL).  Validation of every segment precedes the
- * launch; errors as for bsa_prefill_packed.
+ * one grid.  segments: HOST array of n_segments (1..4) descriptors.  XA_BF16
+ * inputs only.
+ *
+ * Work order: each (segment, query head, query block) row of kept key blocks
+ * is one work item.  Two small kernels on the same stream count every item's
+ * kept blocks and sort the items longest first; the attention workgroups take
+ * items in that order as they start, so the longest rows do not trail at the
+ * end of the grid.  The order decides only which workgroup computes an item:
+ * results do not depend on it.
+ * workspace: at least bsa_prefill_segments_workspace_size(q_len, num_q_heads,
+ * n_segments) bytes of 256-byte aligned device memory, owned by the caller and
+ * used only by this call while it runs (two calls in flight at once need two
+ * workspaces); contents need no initialisation.  XA_EWORKSPACE if missing or
+ * too small.  Validation of every segment precedes the launch; other errors as
+ * for bsa_prefill_packed.
  * ------------------------------------------------------------------------ */
 typedef struct {
   const void* k;               /* [kv_len][num_kv_heads][head_dim] key rows of this segment */
@@ -211,6 +222,10 @@ typedef struct {
   void* out;                   /* out_dtype [q_len][num_q_heads][head_dim] */
   float* lse;                  /* [num_q_heads][q_len] */
 } xa_segment_t;
+
+/* Bytes of the ordering buffers: 256 + 2 * round_up(4 * items, 256) with
+ * items = n_segments * num_q_heads * ceil(q_len / 128); 0 for invalid sizes. */
+size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t n_segments);
 
 xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                                  const void* packed_v, int64_t capacity, xa_dtype_t dtype,

@@ -137,6 +137,27 @@ def test_pack_v_rejects(lib):
                           None) == B.XA_EINVAL
 
 
+def test_segments_workspace(lib):
+    n_items = 2 * 32 * 32
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 2) == 256 + 2 * ((n_items * 4 + 255) // 256 * 256)
+    assert B.bsa_prefill_segments_workspace_size(4000, 32, 1) == 256 + 2 * 4096   # 32 query blocks, ragged
+    assert B.bsa_prefill_segments_workspace_size(0, 32, 2) == 0
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 5) == 0
+    seg = (B.Segment * 1)()
+    seg[0] = B.Segment(FAKE.value, 8 * 128, 128, 4096, 0, 0, None, 0, 0, 0, 0, FAKE2.value, FAKE.value)
+    need = B.bsa_prefill_segments_workspace_size(4096, 32, 1)
+
+    def call(ws, wsb, n=1, dt=B.XA_BF16):
+        return lib.bsa_prefill_segments(FAKE, 32 * 128, 128, FAKE, 8192, dt, 4096, 32, 8, 128, 4096, seg, n, 128,
+                                        0.0, B.XA_BF16, ws, wsb, None)
+    assert call(None, 0) == B.XA_EWORKSPACE
+    assert call(FAKE, need - 1) == B.XA_EWORKSPACE
+    assert call(ctypes.c_void_p(0x100010), need) == B.XA_EWORKSPACE
+    assert call(FAKE, need, n=0) == B.XA_EINVAL
+    assert call(FAKE, need, n=5) == B.XA_EINVAL
+    assert call(FAKE, need, dt=B.XA_F32) == B.XA_EUNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))

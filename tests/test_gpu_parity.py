@@ -244,3 +244,45 @@ def test_segments_in_one_launch():
             O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, np.broadcast_to(row, (hq, nqb, p // 128)), 0, False)]
     for (go, gl), (ro, rl) in zip(outs, refs):
         PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
+
+
+def test_segments_work_order():
+    """The longest-first work order of a segmented launch, read back from its workspace.
+
+    Exact integer checks: every item's kept-tile count equals the mask row's
+    count up to the causal limit (as a multiset over items), the order is a
+    permutation sorted by descending count, and every workgroup took a ticket.
+    """
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, L, p = 8, 2, 128, 1280, 768
+    qd = _rand((L, hq, d), torch.bfloat16, 83).to(DEV)
+    kd = _rand((L, hkv, d), torch.bfloat16, 84).to(DEV)
+    packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
+    B.bsa_pack_v(_rand((L, hkv, d), torch.bfloat16, 85).to(DEV), packed, 0)
+    rng = np.random.default_rng(10)
+    nqb, nkb = (L - p) // 128, L // 128
+    mask = (rng.random((hq, nqb, nkb)) < 0.5).astype(np.uint8)
+    row = (rng.random(p // 128) < 0.5).astype(np.uint8)
+    md, rowd = torch.from_numpy(mask).to(DEV), torch.from_numpy(row).to(DEV).view(1, 1, -1)
+    outs = [(torch.empty(L - p, hq, d, dtype=torch.bfloat16, device=DEV),
+             torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(3)]
+    segs = [dict(k=kd[128:p], kv_start=128, v_token_offset=128, block_mask=md, causal=False,
+                 out=outs[0][0], lse=outs[0][1]),
+            dict(k=kd[p:], kv_start=p, v_token_offset=p, block_mask=md, causal=True, out=outs[1][0], lse=outs[1][1]),
+            dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=rowd, mask_head_stride=0, mask_row_stride=0,
+                 causal=False, out=outs[2][0], lse=outs[2][1])]
+    n = 3 * hq * nqb
+    ws = B.workspace(B.bsa_prefill_segments_workspace_size(L - p, hq, 3), DEV)
+    ws.fill_(0xAB)
+    B.bsa_prefill_segments(qd[p:], packed, p, segs, ws=ws)
+    torch.cuda.synchronize()
+    w32 = ws.cpu().numpy().view(np.int32)
+    arr = (n * 4 + 255) // 256 * 256
+    ticket, weights, order = w32[0], w32[64:64 + n], w32[(256 + arr) // 4:(256 + arr) // 4 + n]
+    expect = [int(mask[h, qb, 1:6].sum()) for h in range(hq) for qb in range(nqb)]
+    expect += [int(mask[h, qb, 6:6 + min(qb + 1, 4)].sum()) for h in range(hq) for qb in range(nqb)]
+    expect += [int(row.sum())] * (hq * nqb)
+    assert ticket == n
+    assert sorted(weights.tolist()) == sorted(expect)
+    assert sorted(order.tolist()) == list(range(n))
+    assert np.all(np.diff(weights[order]) <= 0)
