@@ -11,10 +11,12 @@ effective TFLOP/s on computed blocks, the attention kernel's roofline entry
 oracle timed on one key/value-head group of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-mib N   # plain device copy of N MiB (HBM counter calibration)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +27,13 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.hip")
+
+# HBM bytes per attention launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# passes over this bench (profiles/ holds the summaries and the commands),
+# scaled by the same counters' reading for a plain copy of known size.  Valid
+# only for the attention source they were taken on (sha256 of bsa.hip).
+TRAFFIC = {}
 
 
 def parse():
@@ -35,7 +44,25 @@ def parse():
     ap.add_argument("--workload", default="llama8b_32k_8x4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=1, help="kv-head groups timed for the CPU baseline")
+    ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain device copy of this many MiB")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, five times (counter calibration)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}))
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def count_flops(run):
@@ -121,6 +148,9 @@ def main():
                                    "this build (the path shards by kv-head group, see DESIGN.md)",
                           "n_gpus": a.gpus}))
         sys.exit(2)
+    if a.copy_mib:
+        copy_probe(a.copy_mib)
+        return
     import torch
     from block_sparse_attention_xattn_amd import synthetic
     from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
@@ -214,6 +244,10 @@ def main():
     eff_tflops = (bsa_flops_step + est_flops) / (step_ms * 1e-3) / 1e12
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
+    rec = TRAFFIC.get(a.workload)
+    traffic = None
+    if rec and rec["bsa_sha256"] == source_sha(ATTN_SRC):
+        traffic = rec["hbm_bytes_per_launch"]
 
     out = {
         "metric": "sparse prefill tokens/s per layer (estimate+BSA) at 32K/128K; % bf16 MFMA peak",
@@ -231,11 +265,12 @@ def main():
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
                    "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
                    "block": 128, "chunks_timed": len(run.starts)},
-        "roofline": {"bound": "mfma", "kernel": "bsa_kernel (block-sparse attention)",
+        "roofline": {"bound": "mfma", "kernel": "bsa2_kernel<128, bf16> (block-sparse attention)",
                      "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(bsa_avg_ms, 4), "launches_per_step": n_launch,
-                     "flop_per_launch_avg": bsa_flops_step / n_launch},
+                     "flop_per_launch_avg": bsa_flops_step / n_launch,
+                     "timed_call": "one attention call: work-order count + sort kernels, then the attention kernel"},
         "effective_tflops": round(eff_tflops, 1),
         "effective_frac_of_peak": round(eff_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "density": round(dens, 4),

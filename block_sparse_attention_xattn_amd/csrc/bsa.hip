@@ -379,6 +379,16 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Raw buffer descriptor over [base, base + bytes); loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from descriptor offset voff into LDS: lane L lands at lds + 16 L.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 template <int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   __shared__ int s_item;
@@ -386,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   if (M.order) {
     if (threadIdx.x == 0) s_item = M.order[atomicAdd(M.ticket, 1)];
     __syncthreads();
-    item = s_item;
+    item = __builtin_amdgcn_readfirstlane(s_item);
   }
   int sidx = 0;
   while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
@@ -444,31 +454,40 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   char* kt = smem;
   char* vt = smem + KTB;
 
+  // Byte offsets of this lane's 16-byte pieces inside a K tile and a V^T tile:
+  // the same for every key block, so a block's loads are one uniform base plus
+  // these (the launcher checks that they fit in 32 bits).
+  uint32_t koff[KI], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int lin = (wave * KI + i) * 64 + lane;
+    const int r = lin / KCH;
+    const int ch = (lin % KCH) ^ (r & (KCH - 1));
+    koff[i] = (uint32_t)(((int64_t)r * P.k_tok + ch * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int lin = (wave * VI + i) * 64 + lane;
+    const int r = lin >> 4;
+    const int ch = (lin & 15) ^ (r & 15);
+    voff[i] = (uint32_t)(((int64_t)r * P.vt_pitch + ch * 8) * 2);
+  }
+  // Loads of one key block: a buffer descriptor at the block's first row, these
+  // offsets per lane.  Pieces past the descriptor's extent (rows beyond kv_len)
+  // read as zero; those keys are masked before the softmax.
   auto issue_k = [&](int jb) {
     const int64_t j0 = (int64_t)jb * kBlk;
-    const bf16* base = kg + j0 * P.k_tok;
-    const int rows_left = (int)((P.kv_len - j0) < kBlk ? (P.kv_len - j0) : kBlk);
+    const int64_t rows = P.kv_len - j0 < kBlk ? P.kv_len - j0 : kBlk;
+    const auto rs = tile_rsrc(kg + j0 * P.k_tok, (uint32_t)(((rows - 1) * P.k_tok + D) * 2));
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int inst = wave * KI + i;
-      const int lin = inst * 64 + lane;
-      int r = lin / KCH;
-      const int ch = (lin % KCH) ^ (r & (KCH - 1));
-      r = r < rows_left ? r : rows_left - 1;  // rows past the tail are masked later
-      g2lds16(base + (int64_t)r * P.k_tok + ch * 8, kt + inst * 1024);
-    }
+    for (int i = 0; i < KI; ++i) buf2lds16(rs, koff[i], kt + (wave * KI + i) * 1024);
   };
   auto issue_v = [&](int jb) {
-    const bf16* base = vg + (int64_t)jb * kBlk;
+    const auto rs = tile_rsrc(vg + (int64_t)jb * kBlk, (uint32_t)(((int64_t)(D - 1) * P.vt_pitch + kBlk) * 2));
 #pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int inst = wave * VI + i;
-      const int lin = inst * 64 + lane;
-      const int r = lin >> 4;
-      const int ch = (lin & 15) ^ (r & 15);
-      g2lds16(base + (int64_t)r * P.vt_pitch + ch * 8, vt + inst * 1024);
-    }
+    for (int i = 0; i < VI; ++i) buf2lds16(rs, voff[i], vt + (wave * VI + i) * 1024);
   };
+
 
   for (int64_t seg = 0; seg < jb_end; seg += kListMax) {
     const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
@@ -502,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
       issue_v(s_list[0]);
     }
     for (int it = 0; it < cnt; ++it) {
-      const int jb = s_list[it];
+      const int jb = __builtin_amdgcn_readfirstlane(s_list[it]);
       // K(it) landed (V(it) may still be in flight behind it)
       __builtin_amdgcn_s_waitcnt(0x3f70 | VI);  // vmcnt(VI): only this wave's V loads may remain
       __syncthreads();
@@ -772,32 +791,42 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
 }
 
 // Explicit instantiation helpers used by the ABI layer.
+// bsa2_kernel addresses a lane's pieces of a K / V^T tile with 32-bit byte offsets.
+static bool tile_offsets_fit(const BsaParams* segs, int n_seg, int D) {
+  for (int i = 0; i < n_seg; ++i)
+    if ((127 * segs[i].k_tok + D) * 2 >= ((int64_t)1 << 32) ||
+        ((int64_t)(D - 1) * segs[i].vt_pitch + 128) * 2 >= ((int64_t)1 << 32))
+      return false;
+  return true;
+}
+
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s) {
   if constexpr (!SPLIT && D == 128) {
-    BsaMulti m{};
-    int total = 0;
-    for (int i = 0; i < n_seg; ++i) {
-      m.seg[i] = segs[i];
-      total += segs[i].hq * segs[i].n_qb;
-      m.wg_end[i] = total;
-    }
-    m.n_seg = n_seg;
-    if (total > 0) {
-      if (plan) {
-        hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights);
-        hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
-                           plan->order, plan->ticket);
-        m.order = plan->order;
-        m.ticket = plan->ticket;
+    if (tile_offsets_fit(segs, n_seg, D)) {
+      BsaMulti m{};
+      int total = 0;
+      for (int i = 0; i < n_seg; ++i) {
+        m.seg[i] = segs[i];
+        total += segs[i].hq * segs[i].n_qb;
+        m.wg_end[i] = total;
       }
-      hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+      m.n_seg = n_seg;
+      if (total > 0) {
+        if (plan) {
+          hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights);
+          hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
+                             plan->order, plan->ticket);
+          m.order = plan->order;
+          m.ticket = plan->ticket;
+        }
+        hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+      }
+      return hipGetLastError();
     }
-  } else {
-    for (int i = 0; i < n_seg; ++i)
-      hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(segs[i].hq * segs[i].n_qb), dim3(kThreads), 0, s,
-                         segs[i]);
   }
+  for (int i = 0; i < n_seg; ++i)
+    hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(segs[i].hq * segs[i].n_qb), dim3(kThreads), 0, s, segs[i]);
   return hipGetLastError();
 }
 
