@@ -33,7 +33,12 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.h
 # passes over this bench (profiles/ holds the summaries and the commands),
 # scaled by the same counters' reading for a plain copy of known size.  Valid
 # only for the attention source they were taken on (sha256 of bsa.hip).
-TRAFFIC = {}
+TRAFFIC = {
+    "llama8b_32k_8x4k": {
+        "bsa_sha256": "93e6bec78a6df931fbd2e1965b95992f1ac55ce94f41c4a12a5ad75dc73f65a1",
+        "hbm_bytes_per_launch": 2.3140e9,   # fetch 2.2500e9 (x1.9999) + write 6.398e7 (x1.0), mean of 8 chunks
+    },
+}
 
 
 def parse():
