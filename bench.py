@@ -10,7 +10,8 @@ effective TFLOP/s on computed blocks, the attention kernel's roofline entry
 (HIP events around every attention launch in the timed region) and the CPU
 oracle timed on one key/value-head group of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--stride S] [--threshold T] [--no-cpu-baseline]
+  python bench.py --workload llama8b_64k_sweep --sweep   # one line per (stride, threshold)
   python bench.py --copy-mib N   # plain device copy of N MiB (HBM counter calibration)
 """
 from __future__ import annotations
@@ -36,6 +37,7 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.h
 TRAFFIC = {
     "llama8b_32k_8x4k": {
         "bsa_sha256": "93e6bec78a6df931fbd2e1965b95992f1ac55ce94f41c4a12a5ad75dc73f65a1",
+        "stride": 8, "threshold": 0.95,
         "hbm_bytes_per_launch": 2.3140e9,   # fetch 2.2500e9 (x1.9999) + write 6.398e7 (x1.0), mean of 8 chunks
     },
 }
@@ -47,9 +49,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b_32k_8x4k")
+    ap.add_argument("--stride", type=int, default=None, help="override the workload's stride")
+    ap.add_argument("--threshold", type=float, default=None, help="override the workload's threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=1, help="kv-head groups timed for the CPU baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain device copy of this many MiB")
+    ap.add_argument("--sweep", action="store_true", help="every (stride, threshold) of the workload, one line each")
     return ap.parse_args()
 
 
@@ -77,14 +82,15 @@ def count_flops(run):
     (QK^T and PV), diagonal tiles counted whole; estimate: 2*(d*S) flop per
     visible (reshaped row, reshaped column) pair.
     Returns (attention flops per launch in launch order, estimate flops,
-    density, attention flops split {history, in_chunk}).
+    density, attention flops split {history, in_chunk, useful}); "useful"
+    counts only the causally allowed (query, key) pairs of the computed tiles.
     """
     import numpy as np
     d, S, blk = run.d, run.stride, run.block
     per_tile = 4.0 * d * blk * blk
     fused = run.q.dtype.is_floating_point and run.q.element_size() == 2 and d == 128
     launches = []
-    split = {"history": 0.0, "in_chunk": 0.0}
+    split = {"history": 0.0, "in_chunk": 0.0, "useful": 0.0}
     est = 0.0
     sel = tot = 0
     for b in run.bufs:
@@ -104,6 +110,9 @@ def count_flops(run):
             parts.append(("in_chunk", per_tile * float(m[:, :, cur:].sum())))
         for kind, f in parts:
             split[kind] += f
+        # in-chunk diagonal tiles hold 128*129/2 allowed pairs of 128*128
+        n_diag = hq * nqb
+        split["useful"] += sum(f for _, f in parts) - per_tile * n_diag * (1.0 - (blk + 1) / (2.0 * blk))
         if fused:
             launches.append(sum(f for _, f in parts))
         else:
@@ -156,14 +165,30 @@ def main():
     if a.copy_mib:
         copy_probe(a.copy_mib)
         return
-    import torch
     from block_sparse_attention_xattn_amd import synthetic
-    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
 
-    w = synthetic.WORKLOADS[a.workload]
-    dev = "cuda:0"
-    q, k, v = synthetic.workload_inputs(a.workload)
-    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    base = dict(synthetic.WORKLOADS[a.workload])
+    q, k, v = (t.to("cuda:0") for t in synthetic.workload_inputs(a.workload))
+    if a.sweep:
+        # every (stride, threshold) point of the workload on the same inputs, one line each
+        for stride in base.get("strides", (base.get("stride", 8),)):
+            for tau in base.get("thresholds", (base.get("threshold", 0.9),)):
+                w = dict(base, stride=stride, threshold=tau)
+                print(json.dumps(measure(a, w, q, k, v)), flush=True)
+        return
+    w = dict(base)
+    w["stride"] = a.stride if a.stride is not None else w.get("stride", 8)
+    w["threshold"] = a.threshold if a.threshold is not None else w.get("threshold", 0.9)
+    out = measure(a, w, q, k, v)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups)
+    print(json.dumps(out))
+
+
+def measure(a, w, q, k, v):
+    """Warm up, time a.steps steps of the workload w on resident q, k, v; return the JSON record."""
+    import torch
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
     starts = None
     if "q_start_pos" in w:
         starts = [w["q_start_pos"]]
@@ -184,7 +209,7 @@ def main():
         e.record(stream)
         ev.append((tag, e))
 
-    orig_attend, orig_est, orig_merge, orig_pack = run.attend, run.estimate, run.merge, run.pack
+    orig_est, orig_merge, orig_pack, orig_reduce = run.estimate, run.merge, run.pack, run.reduce
 
     def timed(tag, fn):
         def inner(b):
@@ -208,6 +233,7 @@ def main():
     run.estimate = timed("estimate", orig_est)
     run.merge = timed("merge", orig_merge)
     run.pack = timed("pack", orig_pack)
+    run.reduce = timed("reduce", orig_reduce)
     B.bsa_prefill_packed = wrap(orig_bsa)
     B.bsa_prefill_segments = wrap(orig_seg)
     torch.cuda.synchronize()
@@ -241,6 +267,18 @@ def main():
         parts[kk] /= a.steps
 
     launches, est_flops, dens, split = count_flops(run)
+    # HBM-bound helpers: algorithmic bytes per call over their event time
+    n_merge = sum(1 for b in run.bufs if b.p > 0)
+    hbm = {}
+    if n_merge and parts.get("merge"):
+        c_len = w["chunk"]
+        per_merge = 3 * c_len * w["hq"] * w["d"] * q.element_size() + 3 * w["hq"] * c_len * 4
+        hbm["merge_gbs"] = round(per_merge * n_merge / (parts["merge"] * 1e-3) / 1e9, 1)
+    red = [b for b in run.bufs if b.keep_any is not None]
+    if red and parts.get("reduce"):
+        per_red = sum(b.mask.shape[0] * b.mask.shape[1] * b.keep_any.shape[0] * (w["cache_block"] // 128)
+                      + b.keep_per_head.numel() + b.keep_any.numel() + b.keep_any_blocks.numel() for b in red)
+        hbm["reducer_gbs"] = round(per_red / (parts["reduce"] * 1e-3) / 1e9, 1)
     bsa_flops_step = sum(launches)
     n_launch = len(launches)
     assert len(bsa_durs) == n_launch * a.steps, (len(bsa_durs), n_launch)
@@ -249,9 +287,16 @@ def main():
     eff_tflops = (bsa_flops_step + est_flops) / (step_ms * 1e-3) / 1e12
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
+    if q.dtype == torch.bfloat16 and w["d"] == 128:
+        kernel_name = "bsa2_kernel<128, bf16> (block-sparse attention)"
+        timed_call = "one attention call: work-order count + sort kernels, then the attention kernel"
+    else:
+        kernel_name = f"bsa_kernel<{w['d']}, {'fp32 as bf16 hi/lo' if q.dtype == torch.float32 else 'bf16'}>"
+        timed_call = "one attention call per segment: one kernel"
     rec = TRAFFIC.get(a.workload)
     traffic = None
-    if rec and rec["bsa_sha256"] == source_sha(ATTN_SRC):
+    if rec and rec["bsa_sha256"] == source_sha(ATTN_SRC) and (rec["stride"], rec["threshold"]) == (
+            w["stride"], w["threshold"]):
         traffic = rec["hbm_bytes_per_launch"]
 
     out = {
@@ -270,12 +315,12 @@ def main():
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
                    "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
                    "block": 128, "chunks_timed": len(run.starts)},
-        "roofline": {"bound": "mfma", "kernel": "bsa2_kernel<128, bf16> (block-sparse attention)",
+        "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(bsa_avg_ms, 4), "launches_per_step": n_launch,
                      "flop_per_launch_avg": bsa_flops_step / n_launch,
-                     "timed_call": "one attention call: work-order count + sort kernels, then the attention kernel"},
+                     "timed_call": timed_call},
         "effective_tflops": round(eff_tflops, 1),
         "effective_frac_of_peak": round(eff_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "density": round(dens, 4),
@@ -283,10 +328,10 @@ def main():
         "bsa_gflop_split": {k2: round(v2 / 1e9, 1) for k2, v2 in split.items()},
         "estimate_gflop": round(est_flops / 1e9, 1),
         "bsa_gflop": round(bsa_flops_step / 1e9, 1),
+        "bsa_useful_tflops": round(split["useful"] * a.steps / (sum(bsa_durs) * 1e-3) / 1e12, 1),
+        **hbm,
     }
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups)
-    print(json.dumps(out))
+    return out
 
 
 if __name__ == "__main__":
