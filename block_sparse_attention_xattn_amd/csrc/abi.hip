@@ -189,6 +189,8 @@ extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_he
   sp.lse_part = p.lse_part;
   sp.R = p.R;
   sp.nkb = p.nkb;
+  sp.npow_cap = 1;
+  while (sp.npow_cap < p.nkb) sp.npow_cap <<= 1;
   sp.b = p.b;
   sp.hq = hq;
   sp.n_qb = (int)(q_len / block);

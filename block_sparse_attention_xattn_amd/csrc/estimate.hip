@@ -297,11 +297,15 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
 // (head, query block).
 // ---------------------------------------------------------------------------
 
-constexpr int kSortMax = 8192;
 
+// B = rows of a query block in the reshaped score matrix (block / stride); the
+// per-row loads are unrolled so that each thread's loads are in flight together.
+template <int B>
 __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
-  __shared__ unsigned long long keys[kSortMax];
-  __shared__ uint8_t mrow[kSortMax];
+  // dynamic LDS: npow_cap sort keys, then nkb mask bytes
+  extern __shared__ __attribute__((aligned(16))) unsigned long long sel_dyn[];
+  unsigned long long* keys = sel_dyn;
+  uint8_t* mrow = reinterpret_cast<uint8_t*>(sel_dyn + P.npow_cap);
   __shared__ float row_lse[64];
   __shared__ float red_m[256];
   __shared__ float red_s[256];
@@ -312,25 +316,34 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
   const int tid = threadIdx.x;
   const int h = blockIdx.x / P.n_qb;
   const int qb = blockIdx.x % P.n_qb;
-  const int b = P.b;
+  constexpr int b = B;
   const int64_t diag = P.cur + qb;  // always-kept diagonal block
   const int nvis = (int)diag + 1;   // key blocks 0..diag
   const float* base = P.lse_part + (int64_t)h * P.nkb * P.R + (int64_t)qb * b;
 
   // pass 1: per-row normaliser over key blocks (log2 units)
   {
+    constexpr int nstripe = 256 / b;
+    constexpr int U = 8;  // loads in flight per thread
     const int r = tid % b;
     const int stripe = tid / b;
-    const int nstripe = 256 / b;
     float m = -INFINITY, s = 0.f;
-    for (int kb = stripe; kb < nvis; kb += nstripe) {
-      const float v = base[(int64_t)kb * P.R + r];
-      if (v == -INFINITY) continue;
-      if (v > m) {
-        s = s * fast_exp2(m - v) + 1.f;
-        m = v;
-      } else {
-        s += fast_exp2(v - m);
+    for (int kb0 = stripe; kb0 < nvis; kb0 += nstripe * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kb = kb0 + u * nstripe;
+        v[u] = kb < nvis ? base[(int64_t)kb * P.R + r] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v[u] == -INFINITY) continue;
+        if (v[u] > m) {
+          s = s * fast_exp2(m - v[u]) + 1.f;
+          m = v[u];
+        } else {
+          s += fast_exp2(v[u] - m);
+        }
       }
     }
     red_m[tid] = m;
@@ -358,16 +371,21 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
     float a = 0.f;
     if (kb < nvis) {
       const float* col = base + (int64_t)kb * P.R;
-      for (int r = 0; r < b; ++r) {
-        const float v = col[r];
-        if (v != -INFINITY) a += fast_exp2(v - row_lse[r]);
+#pragma unroll
+      for (int r0 = 0; r0 < b; r0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16 && r0 + r < b; ++r) v[r] = col[r0 + r];
+#pragma unroll
+        for (int r = 0; r < 16 && r0 + r < b; ++r)
+          if (v[r] != -INFINITY) a += fast_exp2(v[r] - row_lse[r0 + r]);
       }
       tsum += a;
     }
     P.scores[((int64_t)h * P.n_qb + qb) * P.nkb + kb] = a;
     const bool forced = kb == 0 || kb == diag;
-    if (kb < kSortMax) mrow[kb] = (kb < nvis && (all || forced)) ? 1 : 0;
-    if (kb < npow && kb < kSortMax) {
+    mrow[kb] = (kb < nvis && (all || forced)) ? 1 : 0;
+    if (kb < npow) {
       const unsigned bits = __float_as_uint(a);
       keys[kb] = (kb < nvis && !forced) ? (((unsigned long long)(0xffffffffu - bits) << 32) | (unsigned)kb)
                                          : ~0ull;
@@ -469,7 +487,19 @@ template hipError_t launch_est_gemm<128, false>(const EstParams&, hipStream_t);
 template hipError_t launch_est_gemm<128, true>(const EstParams&, hipStream_t);
 
 hipError_t launch_est_select(const SelParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(est_select_kernel, dim3(p.hq * p.n_qb), dim3(256), 0, s, p);
+  const dim3 grid(p.hq * p.n_qb);
+  const size_t lds = (size_t)p.npow_cap * 8 + ((size_t)p.nkb + 15) / 16 * 16;
+  auto go = [&](auto kern) {
+    if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+  };
+  switch (p.b) {
+    case 8: go(est_select_kernel<8>); break;
+    case 16: go(est_select_kernel<16>); break;
+    case 32: go(est_select_kernel<32>); break;
+    case 64: go(est_select_kernel<64>); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

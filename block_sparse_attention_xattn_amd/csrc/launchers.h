@@ -45,7 +45,8 @@ struct EstParams {
 struct SelParams {
   const float* lse_part;
   int R, nkb, b, hq, n_qb;
-  int64_t cur;  // key blocks before the chunk (q_start / 128)
+  int npow_cap;  // smallest power of two >= nkb (sort buffer length)
+  int64_t cur;   // key blocks before the chunk (q_start / 128)
   float threshold;
   float* scores;  // [hq][n_qb][nkb]
   uint8_t* mask;  // [hq][n_qb][nkb]
