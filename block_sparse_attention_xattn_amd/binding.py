@@ -70,7 +70,7 @@ def _declare(lib):
     lib.bsa_prefill_segments.argtypes = [P, I64, I64, P, I64, ctypes.c_int, I64, I32, I32, I32, I64,
                                          ctypes.POINTER(Segment), I32, I32, F, ctypes.c_int, P, SZ, P]
     lib.bsa_prefill_segments_workspace_size.restype = SZ
-    lib.bsa_prefill_segments_workspace_size.argtypes = [I64, I32, I32]
+    lib.bsa_prefill_segments_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -255,8 +255,8 @@ def bsa_prefill_packed(q, k, packed: PackedV, v_token_offset: int, q_start_pos: 
     return out, lse
 
 
-def bsa_prefill_segments_workspace_size(q_len: int, num_q_heads: int, n_segments: int) -> int:
-    return int(lib().bsa_prefill_segments_workspace_size(q_len, num_q_heads, n_segments))
+def bsa_prefill_segments_workspace_size(q_len: int, num_q_heads: int, head_dim: int, n_segments: int) -> int:
+    return int(lib().bsa_prefill_segments_workspace_size(q_len, num_q_heads, head_dim, n_segments))
 
 
 def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax_scale: float = 0.0, block: int = 128,
@@ -284,7 +284,7 @@ def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax
         keep.append((g["out"], g["lse"]))
     odt = _dtype_code(segments[0]["out"])
     if ws is None:
-        ws = workspace(bsa_prefill_segments_workspace_size(q_len, hq, len(segments)), q.device)
+        ws = workspace(bsa_prefill_segments_workspace_size(q_len, hq, d, len(segments)), q.device)
     _check(lib().bsa_prefill_segments(_ptr(q), q.stride(0), q.stride(1), _ptr(packed.buf), packed.capacity, dt,
                                       q_len, hq, packed.hkv, d, q_start_pos, arr, len(segments), block,
                                       float(softmax_scale), odt, _ptr(ws), ws.numel(), _stream(stream)))

@@ -314,6 +314,19 @@ xa_status_t split_qk(const char* fn, const void* q, int64_t& q_tok, int64_t& q_h
   return XA_OK;
 }
 
+// Attention workgroups resident at once on the current device (two per compute unit).
+int resident_workgroups() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
+}
+
 xa_status_t run_bsa(const char* fn, const BsaParams* segs, int n, int32_t d, xa_dtype_t dtype, xa_dtype_t out_dtype,
                     hipStream_t s, const BsaPlan* plan = nullptr) {
   const bool split = dtype == XA_F32;
@@ -453,11 +466,12 @@ extern "C" xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok, int64_t 
                     reinterpret_cast<hipStream_t>(stream));
 }
 
-extern "C" size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t n_segments) {
-  if (q_len <= 0 || num_q_heads <= 0 || n_segments < 1 || n_segments > kMaxSegments) return 0;
+extern "C" size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t head_dim,
+                                                      int32_t n_segments) {
+  if (q_len <= 0 || num_q_heads <= 0 || head_dim <= 0 || n_segments < 1 || n_segments > kMaxSegments) return 0;
   const int64_t n_items = (int64_t)n_segments * num_q_heads * ((q_len + 127) / 128);
-  if (n_items > (int64_t)1 << 30) return 0;
-  return bsa_plan_bytes(n_items);
+  if (n_items > (int64_t)1 << 28) return 0;
+  return bsa_plan_layout(n_items, head_dim).total;
 }
 
 extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_t q_head, const void* packed_v,
@@ -484,15 +498,25 @@ extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_
       return fail(XA_EINVAL, "%s: segment %d: packed tokens [%lld, %lld) outside the capacity %lld", fn, i,
                   (long long)g.v_token_offset, (long long)(g.v_token_offset + g.kv_len), (long long)pitch);
   }
-  const size_t need = bsa_prefill_segments_workspace_size(q_len, hq, n_segments);
+  const size_t need = bsa_prefill_segments_workspace_size(q_len, hq, d, n_segments);
   if (need == 0) return fail(XA_EINVAL, "%s: too many work items (q_len %lld, %d heads)", fn, (long long)q_len, hq);
   if (!workspace || (uintptr_t)workspace % 256 != 0 || ws_bytes < need)
     return fail(XA_EWORKSPACE, "%s: needs a 256-byte aligned workspace of %zu bytes (got %zu at %p)", fn, need,
                 ws_bytes, workspace);
   char* w = static_cast<char*>(workspace);
   const int64_t n_items = (int64_t)n_segments * hq * ((q_len + 127) / 128);
-  const size_t arr = ((size_t)n_items * 4 + 255) / 256 * 256;
-  const BsaPlan plan{reinterpret_cast<int*>(w + 256), reinterpret_cast<int*>(w + 256 + arr), reinterpret_cast<int*>(w)};
+  const BsaPlanLayout L = bsa_plan_layout(n_items, d);
+  BsaPlan plan{};
+  plan.ctl = reinterpret_cast<int*>(w + L.ctl);
+  plan.weights = reinterpret_cast<int*>(w + L.weights);
+  plan.mid = reinterpret_cast<int*>(w + L.mid);
+  plan.slot = reinterpret_cast<int*>(w + L.slot);
+  plan.split_items = reinterpret_cast<int*>(w + L.split_items);
+  plan.order = reinterpret_cast<int*>(w + L.order);
+  plan.part_o = reinterpret_cast<float*>(w + L.part_o);
+  plan.part_lse = reinterpret_cast<float*>(w + L.part_lse);
+  plan.max_split = L.max_split;
+  plan.slots = resident_workgroups();
   BsaParams segs[kMaxSegments];
   const bf16* vh = static_cast<const bf16*>(packed_v);
   for (int i = 0; i < n_segments; ++i) {

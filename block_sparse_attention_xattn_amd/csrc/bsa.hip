@@ -392,11 +392,21 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
 template <int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   __shared__ int s_item;
-  int item = (int)blockIdx.x;
+  int item = (int)blockIdx.x, part = 0;
   if (M.order) {
-    if (threadIdx.x == 0) s_item = M.order[atomicAdd(M.ticket, 1)];
+    // the grid has room for every possible split; only items + splits workgroups take a ticket
+    // (the split count is read only by the workgroups past the item count)
+    const int n_items = M.wg_end[M.n_seg - 1];
+    if ((int)blockIdx.x >= n_items && (int)blockIdx.x >= n_items + M.ctl[2]) return;
+    if (threadIdx.x == 0) {
+      const int t = atomicAdd(&M.ctl[0], 1);
+      s_item = t < M.ctl[1] ? M.order[t] : -1;
+    }
     __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(s_item);
+    const int e = __builtin_amdgcn_readfirstlane(s_item);
+    if (e < 0) return;  // every entry already taken
+    item = e >> 2;
+    part = e & 3;
   }
   int sidx = 0;
   while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
@@ -447,6 +457,9 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
     const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
     jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
   }
+  int64_t jb_lo = 0;
+  if (part == 1) jb_end = M.mid[item];  // first half of a split item
+  if (part == 2) jb_lo = M.mid[item];   // second half
   const uint8_t* mrow =
       P.mask ? P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
   const bf16* kg = P.k_hi + (int64_t)kvh * P.k_head;
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   };
 
 
-  for (int64_t seg = 0; seg < jb_end; seg += kListMax) {
+  for (int64_t seg = jb_lo; seg < jb_end; seg += kListMax) {
     const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
     {
       // each wave scans a quarter of the segment: count, exchange, write
@@ -592,6 +605,21 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   if (l_row > 0.f) {
     inv = 1.f / l_row;
     lse_v = (m_run * c + log2f(l_row)) * kLn2;
+  }
+  if (part != 0) {
+    // half of a split item: fp32 partial result, merged by split_merge_kernel
+    const size_t ps = (size_t)(2 * M.slot[item] + part - 1) * kBlk + wave * 32 + n;
+    float* po = M.part_o + ps * D;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hh;
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[md][g4 * 4] * inv, o[md][g4 * 4 + 1] * inv,
+                                                   o[md][g4 * 4 + 2] * inv, o[md][g4 * 4 + 3] * inv};
+      }
+    if (hh == 0) M.part_lse[ps] = lse_v;
+    return;
   }
   OutT* out = reinterpret_cast<OutT*>(P.out);
   const int64_t obase = row * ((int64_t)P.hq * D) + (int64_t)h * D;
@@ -712,58 +740,83 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
-// Longest-first ordering of a segmented launch.  The kept-tile count of a
-// work item's row varies several-fold across heads and query blocks; taking
-// items in dispatch order leaves long rows for the end of the grid.  Two small
-// kernels count each item's kept tiles and sort the item ids by descending
-// count (counting sort in one workgroup); the attention workgroups then take
-// items in that order as they start (greedy longest-processing-time list
-// scheduling).  Ordering changes only which workgroup computes an item.
+// Work order of a segmented launch.  The kept-tile count of a work item's row
+// varies several-fold across heads and query blocks; taking items in dispatch
+// order leaves long rows for the end of the grid, and a row longer than the
+// mean load per workgroup slot bounds the whole launch by itself.  Two small
+// kernels count each item's kept tiles, split every item longer than that mean
+// into two halves at its median kept block, and sort the entries by
+// descending count (counting sort in one workgroup); the attention workgroups
+// take entries in that order as they start (greedy longest-processing-time
+// list scheduling), and a last kernel merges the two halves of each split item
+// by their LSE.  The order decides only which workgroup computes what.
 constexpr int kPlanBins = 4096;  // counts >= kPlanBins-1 share the last bin
+constexpr int kMinSplit = 32;    // items with fewer kept tiles are never split
 
-// One wave per work item: kept key blocks before the causal limit.
-__global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items, int* __restrict__ weights) {
-  const int item = (int)blockIdx.x * 4 + wave_id();
-  const int lane = lane_id();
-  if (item >= n_items) return;
-  int sidx = 0;
+__device__ __forceinline__ void item_span(const BsaMulti& M, int item, int& sidx, int& h, int& qb, int64_t& jb_end) {
+  sidx = 0;
   while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
   const BsaParams& P = M.seg[sidx];
-  const int bid = item - (sidx ? M.wg_end[sidx - 1] : 0);
-  int h, qb;
-  bsa_decode(bid, P.group, P.hkv, P.n_qb, h, qb);
+  bsa_decode(item - (sidx ? M.wg_end[sidx - 1] : 0), P.group, P.hkv, P.n_qb, h, qb);
   const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
-  int64_t jb_end = nkb;
+  jb_end = nkb;
   if (P.causal) {
     const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
     jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
   }
+}
+
+// One wave per work item: kept key blocks below the causal limit, and the key
+// block of its (count / 2)-th kept block (0-based), where a second half starts.
+__global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items, int* __restrict__ weights,
+                                                         int* __restrict__ mid) {
+  const int item = (int)blockIdx.x * 4 + wave_id();
+  const int lane = lane_id();
+  if (item >= n_items) return;
+  int sidx, h, qb;
+  int64_t jb_end;
+  item_span(M, item, sidx, h, qb, jb_end);
+  const BsaParams& P = M.seg[sidx];
   int cnt;
+  int64_t half_at;
   if (P.mask == nullptr) {
-    cnt = jb_end < kPlanBins ? (int)jb_end : kPlanBins;
+    cnt = (int)jb_end;
+    half_at = jb_end / 2;
   } else {
     const uint8_t* mrow = P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (P.kv_start / kBlk - P.mask_off);
     cnt = 0;
     for (int64_t jb = lane; jb < jb_end; jb += 64) cnt += mrow[jb] != 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    const int target = cnt / 2;
+    half_at = jb_end;
+    int run = 0;
+    for (int64_t base = 0; base < jb_end; base += 64) {
+      const int64_t jb = base + lane;
+      const bool kept = jb < jb_end && mrow[jb] != 0;
+      const uint64_t bal = __ballot(kept);
+      const int c = __popcll(bal);
+      if (run + c > target) {
+        const int before = __popcll(bal & ((1ull << lane) - 1));
+        const uint64_t hit = __ballot(kept && run + before == target);
+        half_at = base + __ffsll((unsigned long long)hit) - 1;
+        break;
+      }
+      run += c;
+    }
   }
-  if (lane == 0) weights[item] = cnt;
+  if (lane == 0) {
+    weights[item] = cnt;
+    mid[item] = (int)half_at;
+  }
 }
 
-// One workgroup: order[] = item ids by descending weight; ticket = 0.
-__global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int* __restrict__ weights,
-                                                         int* __restrict__ order, int* __restrict__ ticket) {
-  __shared__ int bins[kPlanBins];
-  __shared__ int wsum[16];
+// Exclusive scan of kPlanBins bins from the highest bin down (1024 threads,
+// four bins each); bins[b] becomes the number of entries in higher bins.
+__device__ __forceinline__ void scan_bins_desc(int* bins, int* wsum) {
   const int t = (int)threadIdx.x;
   const int lane = lane_id();
   const int wave = t >> 6;
-  for (int b = t; b < kPlanBins; b += 1024) bins[b] = 0;
-  __syncthreads();
-  for (int i = t; i < n_items; i += 1024) atomicAdd(&bins[min(weights[i], kPlanBins - 1)], 1);
-  __syncthreads();
-  // exclusive scan from the highest bin down: thread t owns bins top-4t .. top-4t-3
   int v[4], own = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -786,8 +839,134 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
     run += v[j];
   }
   __syncthreads();
-  for (int i = t; i < n_items; i += 1024) order[atomicAdd(&bins[min(weights[i], kPlanBins - 1)], 1)] = i;
-  if (t == 0) *ticket = 0;
+}
+
+// One workgroup: choose the items to split (count above total / slots and at
+// least kMinSplit, the longest of them while their whole count bin fits in
+// max_split), assign their partial slots, write the entries longest first and
+// reset the ticket.
+__global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int* __restrict__ weights,
+                                                         int* __restrict__ order, int* __restrict__ ctl,
+                                                         int* __restrict__ slot, int* __restrict__ split_items,
+                                                         int max_split, int slots) {
+  __shared__ int cand[kPlanBins];   // split candidates per count bin
+  __shared__ int above[kPlanBins];  // candidates in higher bins
+  __shared__ int bins[kPlanBins];   // entries per bin, then their write positions
+  __shared__ int wsum[16];
+  __shared__ long long wtot[16];
+  __shared__ int s_nsplit;
+  const int t = (int)threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t >> 6;
+  long long tot = 0;
+  for (int i = t; i < n_items; i += 1024) tot += weights[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+  if (lane == 0) wtot[wave] = tot;
+  for (int b = t; b < kPlanBins; b += 1024) {
+    cand[b] = 0;
+    bins[b] = 0;
+  }
+  if (t == 0) s_nsplit = 0;
+  __syncthreads();
+  long long all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) all += wtot[w];
+  const long long thr = all / (slots > 0 ? slots : 1);
+  // halves of fewer than 16 tiles cost more in per-item overhead and merging than they balance
+  auto candidate = [&](int w) { return w >= kMinSplit && (long long)w > thr; };
+  for (int i = t; i < n_items; i += 1024) {
+    const int w = weights[i];
+    if (candidate(w)) atomicAdd(&cand[min(w, kPlanBins - 1)], 1);
+  }
+  __syncthreads();
+  for (int b = t; b < kPlanBins; b += 1024) above[b] = cand[b];
+  __syncthreads();
+  scan_bins_desc(above, wsum);
+  auto split = [&](int w) {
+    const int b = min(w, kPlanBins - 1);
+    return candidate(w) && above[b] + cand[b] <= max_split;
+  };
+  for (int i = t; i < n_items; i += 1024) {
+    const int w = weights[i];
+    if (split(w)) {
+      atomicAdd(&bins[min(w / 2, kPlanBins - 1)], 1);
+      atomicAdd(&bins[min(w - w / 2, kPlanBins - 1)], 1);
+    } else {
+      atomicAdd(&bins[min(w, kPlanBins - 1)], 1);
+    }
+  }
+  __syncthreads();
+  scan_bins_desc(bins, wsum);
+  for (int i = t; i < n_items; i += 1024) {
+    const int w = weights[i];
+    if (split(w)) {
+      const int k = atomicAdd(&s_nsplit, 1);
+      slot[i] = k;
+      split_items[k] = i;
+      order[atomicAdd(&bins[min(w / 2, kPlanBins - 1)], 1)] = i * 4 + 1;
+      order[atomicAdd(&bins[min(w - w / 2, kPlanBins - 1)], 1)] = i * 4 + 2;
+    } else {
+      order[atomicAdd(&bins[min(w, kPlanBins - 1)], 1)] = i * 4;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    ctl[0] = 0;
+    ctl[1] = n_items + s_nsplit;
+    ctl[2] = s_nsplit;
+  }
+}
+
+// LSE merge of the two halves of split item k (partial slot k) into its
+// segment's out and lse (both -inf: out 0, lse -inf).
+template <int D, typename OutT>
+__device__ void split_merge_one(const BsaMulti& M, int k) {
+  const int item = M.split_items[k];
+  int sidx, h, qb;
+  int64_t jb_end;
+  item_span(M, item, sidx, h, qb, jb_end);
+  const BsaParams& P = M.seg[sidx];
+  const float* la = M.part_lse + (size_t)(2 * k) * kBlk;
+  const float* lb = la + kBlk;
+  const float* oa = M.part_o + (size_t)(2 * k) * kBlk * D;
+  const float* ob = oa + (size_t)kBlk * D;
+  OutT* out = reinterpret_cast<OutT*>(P.out);
+  for (int e = (int)threadIdx.x; e < kBlk * (D / 4); e += 256) {
+    const int r = e / (D / 4);
+    const int c = (e % (D / 4)) * 4;
+    const float a = la[r], b = lb[r];
+    const float m = fmaxf(a, b);
+    float wa = 0.f, wb = 0.f, lse = -INFINITY;
+    if (m != -INFINITY) {
+      wa = expf(a - m);
+      wb = expf(b - m);
+      lse = m + logf(wa + wb);
+      const float inv = 1.f / (wa + wb);
+      wa *= inv;
+      wb *= inv;
+    }
+    const f32x4 x = *reinterpret_cast<const f32x4*>(oa + (size_t)r * D + c);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(ob + (size_t)r * D + c);
+    const int64_t row = (int64_t)qb * kBlk + r;
+    OutT* dst = out + row * ((int64_t)P.hq * D) + (int64_t)h * D + c;
+    if constexpr (sizeof(OutT) == 2) {
+      bf16x4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pk[j] = (bf16)(x[j] * wa + y[j] * wb);
+      *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pk);
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{x[0] * wa + y[0] * wb, x[1] * wa + y[1] * wb, x[2] * wa + y[2] * wb,
+                                            x[3] * wa + y[3] * wb};
+    }
+    if (c == 0) P.lse[(int64_t)h * P.q_len + row] = lse;
+  }
+}
+
+// Split halves are merged by a small grid that strides over the slots in use.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void split_merge_kernel(BsaMulti M) {
+  for (int k = (int)blockIdx.x; k < M.ctl[2]; k += (int)gridDim.x) split_merge_one<D, OutT>(M, k);
 }
 
 // Explicit instantiation helpers used by the ABI layer.
@@ -813,14 +992,24 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
       }
       m.n_seg = n_seg;
       if (total > 0) {
+        int grid = total;
         if (plan) {
-          hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights);
+          hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights,
+                             plan->mid);
           hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
-                             plan->order, plan->ticket);
+                             plan->order, plan->ctl, plan->slot, plan->split_items, plan->max_split, plan->slots);
           m.order = plan->order;
-          m.ticket = plan->ticket;
+          m.ctl = plan->ctl;
+          m.mid = plan->mid;
+          m.slot = plan->slot;
+          m.split_items = plan->split_items;
+          m.part_o = plan->part_o;
+          m.part_lse = plan->part_lse;
+          grid = total + plan->max_split;  // entries: items plus halves of split items
         }
-        hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(total), dim3(256), 0, s, m);
+        hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(grid), dim3(256), 0, s, m);
+        if (plan && plan->max_split > 0)
+          hipLaunchKernelGGL((split_merge_kernel<D, OutT>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
       }
       return hipGetLastError();
     }

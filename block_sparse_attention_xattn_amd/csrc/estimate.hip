@@ -490,7 +490,7 @@ hipError_t launch_est_select(const SelParams& p, hipStream_t s) {
   const dim3 grid(p.hq * p.n_qb);
   const size_t lds = (size_t)p.npow_cap * 8 + ((size_t)p.nkb + 15) / 16 * 16;
   auto go = [&](auto kern) {
-    if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 65536) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
   };
   switch (p.b) {

@@ -55,27 +55,60 @@ struct SelParams {
 // Up to kMaxSegments attention problems sharing Q, heads and packed V, run as
 // one grid.  Work item i (one (head, query block) of one segment) belongs to
 // segment s when wg_end[s-1] <= i < wg_end[s].  Without an order, workgroup b
-// runs item b; with one, each workgroup takes the next ticket t as it starts
-// and runs item order[t].
+// runs item b whole.  With one, each workgroup takes the next ticket t as it
+// starts and runs entry order[t] = item * 4 + part: part 0 is the whole item,
+// parts 1 and 2 the key blocks before / from mid[item] of a split item, whose
+// normalised partial results go to partial slot slot[item] and are merged
+// afterwards.
 constexpr int kMaxSegments = 4;
+constexpr int kMaxSplit = 512;  // items split in two per call, at most
 struct BsaMulti {
   BsaParams seg[kMaxSegments];
   int wg_end[kMaxSegments];
   int n_seg;
-  const int* order;  // item ids, longest kept-tile list first (or null)
-  int* ticket;       // start counter, zeroed by the ordering kernel
+  const int* order;        // entries, longest first (null: no order)
+  int* ctl;                // [0] next ticket, [1] entries, [2] split items
+  const int* mid;          // [items] first key block (segment-relative) of a split item's second half
+  const int* slot;         // [items] partial slot of a split item
+  const int* split_items;  // [max_split] item of each partial slot
+  float* part_o;           // [max_split][2][128][D] normalised partial outputs
+  float* part_lse;         // [max_split][2][128] their LSE (natural log)
 };
 
-// Device buffers for the longest-first ordering of a segmented launch.
+// Device buffers of the work order of a segmented launch.
 struct BsaPlan {
-  int* weights;  // [n_items] kept tiles per item
-  int* order;    // [n_items]
-  int* ticket;
+  int* ctl;
+  int* weights;  // [items] kept key blocks
+  int* mid;
+  int* slot;
+  int* split_items;
+  int* order;    // [items + max_split]
+  float* part_o;
+  float* part_lse;
+  int max_split;  // min(items, kMaxSplit)
+  int slots;      // workgroups resident at once; items above total / slots are split
 };
-// Bytes of the ordering buffers for n_items work items (ticket, weights, order).
-inline size_t bsa_plan_bytes(int64_t n_items) {
-  const size_t a = ((size_t)n_items * 4 + 255) / 256 * 256;
-  return 256 + 2 * a;
+
+// Byte layout of the work-order workspace for n_items items of head_dim d.
+struct BsaPlanLayout {
+  size_t ctl, weights, mid, slot, split_items, order, part_o, part_lse, total;
+  int max_split;
+};
+inline BsaPlanLayout bsa_plan_layout(int64_t n_items, int d) {
+  auto a = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  BsaPlanLayout L{};
+  L.max_split = (int)(n_items < kMaxSplit ? n_items : kMaxSplit);
+  size_t o = 0;
+  L.ctl = o;          o += 256;
+  L.weights = o;      o += a((size_t)n_items * 4);
+  L.mid = o;          o += a((size_t)n_items * 4);
+  L.slot = o;         o += a((size_t)n_items * 4);
+  L.split_items = o;  o += a((size_t)L.max_split * 4);
+  L.order = o;        o += a((size_t)(n_items + L.max_split) * 4);
+  L.part_o = o;       o += a((size_t)L.max_split * 2 * 128 * d * 4);
+  L.part_lse = o;     o += a((size_t)L.max_split * 2 * 128 * 4);
+  L.total = o;
+  return L;
 }
 
 template <int D, bool SPLIT, typename OutT>

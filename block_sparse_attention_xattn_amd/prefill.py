@@ -67,7 +67,7 @@ class ChunkedPrefill:
         bsa_ws = B.bsa_prefill_packed_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
         self.est_ws = B.workspace(est_ws, dev)
         self.bsa_ws = B.workspace(bsa_ws, dev) if bsa_ws > 0 else None
-        self.seg_ws = B.workspace(B.bsa_prefill_segments_workspace_size(chunk, self.hq, 2), dev)
+        self.seg_ws = B.workspace(B.bsa_prefill_segments_workspace_size(chunk, self.hq, self.d, 2), dev)
         self.packed = B.PackedV(self.L, self.hkv, self.d, q.dtype, dev)
         self.out = torch.empty(self.L, self.hq, self.d, dtype=self.out_dtype, device=dev)
         self.bufs = []

@@ -200,16 +200,21 @@ xa_status_t bsa_prefill_packed(const void* q, int64_t q_tok_stride, int64_t q_he
  *
  * Work order: each (segment, query head, query block) row of kept key blocks
  * is one work item.  Two small kernels on the same stream count every item's
- * kept blocks and sort the items longest first; the attention workgroups take
- * items in that order as they start, so the longest rows do not trail at the
- * end of the grid.  The order decides only which workgroup computes an item:
- * results do not depend on it.
+ * kept blocks, split each item longer than the mean load per resident
+ * workgroup (up to 512 items) into two halves at its median kept block, and
+ * sort the entries longest first; the attention workgroups take entries in
+ * that order as they start, so no long row trails at the end of the grid, and
+ * a last kernel merges each split item's halves by their LSE (as attn_merge
+ * does).  The order decides only which workgroup computes what: results equal
+ * those of the unsplit computation up to fp32 rounding.
  * workspace: at least bsa_prefill_segments_workspace_size(q_len, num_q_heads,
- * n_segments) bytes of 256-byte aligned device memory, owned by the caller and
- * used only by this call while it runs (two calls in flight at once need two
- * workspaces); contents need no initialisation.  XA_EWORKSPACE if missing or
- * too small.  Validation of every segment precedes the launch; other errors as
- * for bsa_prefill_packed.
+ * head_dim, n_segments) bytes of 256-byte aligned device memory (the order
+ * plus fp32 partial results of up to 512 split items: 64.5 MiB at head_dim
+ * 128 once there are 512 or more items), owned by the caller and used only by
+ * this call while it runs (two calls in flight at once need two workspaces);
+ * contents need no initialisation.  XA_EWORKSPACE if missing or too small.
+ * Validation of every segment precedes the launch; other errors as for
+ * bsa_prefill_packed.
  * ------------------------------------------------------------------------ */
 typedef struct {
   const void* k;               /* [kv_len][num_kv_heads][head_dim] key rows of this segment */
@@ -223,9 +228,10 @@ typedef struct {
   float* lse;                  /* [num_q_heads][q_len] */
 } xa_segment_t;
 
-/* Bytes of the ordering buffers: 256 + 2 * round_up(4 * items, 256) with
- * items = n_segments * num_q_heads * ceil(q_len / 128); 0 for invalid sizes. */
-size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t n_segments);
+/* Bytes of the work-order workspace for items = n_segments * num_q_heads *
+ * ceil(q_len / 128) work items; 0 for invalid sizes. */
+size_t bsa_prefill_segments_workspace_size(int64_t q_len, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t n_segments);
 
 xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                                  const void* packed_v, int64_t capacity, xa_dtype_t dtype,

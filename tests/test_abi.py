@@ -137,15 +137,25 @@ def test_pack_v_rejects(lib):
                           None) == B.XA_EINVAL
 
 
+def _plan_bytes(n_items, d):
+    a = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    ms = min(n_items, 512)
+    return (256 + 3 * a(4 * n_items) + a(4 * ms) + a(4 * (n_items + ms)) + a(ms * 2 * 128 * d * 4)
+            + a(ms * 2 * 128 * 4))
+
+
 def test_segments_workspace(lib):
-    n_items = 2 * 32 * 32
-    assert B.bsa_prefill_segments_workspace_size(4096, 32, 2) == 256 + 2 * ((n_items * 4 + 255) // 256 * 256)
-    assert B.bsa_prefill_segments_workspace_size(4000, 32, 1) == 256 + 2 * 4096   # 32 query blocks, ragged
-    assert B.bsa_prefill_segments_workspace_size(0, 32, 2) == 0
-    assert B.bsa_prefill_segments_workspace_size(4096, 32, 5) == 0
+    # ticket/counters, per-item counts, medians, slots; split items; entries; fp32 partials of split items
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 128, 2) == _plan_bytes(2 * 32 * 32, 128)
+    assert B.bsa_prefill_segments_workspace_size(4000, 32, 128, 1) == _plan_bytes(32 * 32, 128)  # ragged
+    assert B.bsa_prefill_segments_workspace_size(1024, 8, 128, 2) == _plan_bytes(128, 128)      # < 512 items
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 128, 2) < 70 * 2 ** 20
+    assert B.bsa_prefill_segments_workspace_size(0, 32, 128, 2) == 0
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 128, 5) == 0
+    assert B.bsa_prefill_segments_workspace_size(4096, 32, 0, 2) == 0
     seg = (B.Segment * 1)()
     seg[0] = B.Segment(FAKE.value, 8 * 128, 128, 4096, 0, 0, None, 0, 0, 0, 0, FAKE2.value, FAKE.value)
-    need = B.bsa_prefill_segments_workspace_size(4096, 32, 1)
+    need = B.bsa_prefill_segments_workspace_size(4096, 32, 128, 1)
 
     def call(ws, wsb, n=1, dt=B.XA_BF16):
         return lib.bsa_prefill_segments(FAKE, 32 * 128, 128, FAKE, 8192, dt, 4096, 32, 8, 128, 4096, seg, n, 128,

@@ -247,24 +247,30 @@ def test_segments_in_one_launch():
 
 
 def test_segments_work_order():
-    """The longest-first work order of a segmented launch, read back from its workspace.
+    """The work order of a segmented launch, read back from its workspace.
 
     Exact integer checks: every item's kept-tile count equals the mask row's
-    count up to the causal limit (as a multiset over items), the order is a
-    permutation sorted by descending count, and every workgroup took a ticket.
+    count up to the causal limit (as a multiset over items); the split items
+    are the ones of at least 32 tiles longer than total / (2 x compute units)
+    (none here: rows of at most 10 blocks), each with a median inside its row;
+    the entries are the unsplit items once (part 0) and the split items twice
+    (parts 1 and 2), sorted by descending count, and every entry was taken (the
+    ticket passed the entry count).  The outputs of this call match the oracle.
     """
     from block_sparse_attention_xattn_amd import binding as B
     hq, hkv, d, L, p = 8, 2, 128, 1280, 768
-    qd = _rand((L, hq, d), torch.bfloat16, 83).to(DEV)
-    kd = _rand((L, hkv, d), torch.bfloat16, 84).to(DEV)
+    q = _rand((L, hq, d), torch.bfloat16, 83)
+    k = _rand((L, hkv, d), torch.bfloat16, 84)
+    v = _rand((L, hkv, d), torch.bfloat16, 85)
+    qd, kd = q.to(DEV), k.to(DEV)
     packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
-    B.bsa_pack_v(_rand((L, hkv, d), torch.bfloat16, 85).to(DEV), packed, 0)
+    B.bsa_pack_v(v.to(DEV), packed, 0)
     rng = np.random.default_rng(10)
     nqb, nkb = (L - p) // 128, L // 128
     mask = (rng.random((hq, nqb, nkb)) < 0.5).astype(np.uint8)
     row = (rng.random(p // 128) < 0.5).astype(np.uint8)
     md, rowd = torch.from_numpy(mask).to(DEV), torch.from_numpy(row).to(DEV).view(1, 1, -1)
-    outs = [(torch.empty(L - p, hq, d, dtype=torch.bfloat16, device=DEV),
+    outs = [(torch.empty(L - p, hq, d, dtype=torch.float32, device=DEV),
              torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(3)]
     segs = [dict(k=kd[128:p], kv_start=128, v_token_offset=128, block_mask=md, causal=False,
                  out=outs[0][0], lse=outs[0][1]),
@@ -272,17 +278,74 @@ def test_segments_work_order():
             dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=rowd, mask_head_stride=0, mask_row_stride=0,
                  causal=False, out=outs[2][0], lse=outs[2][1])]
     n = 3 * hq * nqb
-    ws = B.workspace(B.bsa_prefill_segments_workspace_size(L - p, hq, 3), DEV)
+    ws = B.workspace(B.bsa_prefill_segments_workspace_size(L - p, hq, d, 3), DEV)
     ws.fill_(0xAB)
     B.bsa_prefill_segments(qd[p:], packed, p, segs, ws=ws)
     torch.cuda.synchronize()
+    a = lambda b: (b + 255) // 256 * 256  # noqa: E731
     w32 = ws.cpu().numpy().view(np.int32)
-    arr = (n * 4 + 255) // 256 * 256
-    ticket, weights, order = w32[0], w32[64:64 + n], w32[(256 + arr) // 4:(256 + arr) // 4 + n]
+    ms = min(n, 512)
+    off = 256
+    ctl = w32[0:3]
+    weights = w32[off // 4:off // 4 + n]; off += a(4 * n)
+    mids = w32[off // 4:off // 4 + n]; off += a(4 * n)
+    off += a(4 * n)  # slots
+    off += a(4 * ms)  # split items
+    n_split = int(ctl[2])
+    order = w32[off // 4:off // 4 + n + n_split]
     expect = [int(mask[h, qb, 1:6].sum()) for h in range(hq) for qb in range(nqb)]
     expect += [int(mask[h, qb, 6:6 + min(qb + 1, 4)].sum()) for h in range(hq) for qb in range(nqb)]
     expect += [int(row.sum())] * (hq * nqb)
-    assert ticket == n
     assert sorted(weights.tolist()) == sorted(expect)
-    assert sorted(order.tolist()) == list(range(n))
-    assert np.all(np.diff(weights[order]) <= 0)
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    thr = int(weights.sum()) // slots
+    split = {i for i in range(n) if weights[i] >= 32 and weights[i] > thr}
+    assert ctl[1] == n + n_split and n_split == len(split) and ctl[0] >= ctl[1]
+    items, parts = order // 4, order % 4
+    assert {int(i) for i, pt in zip(items, parts) if pt == 0} == set(range(n)) - split
+    for pt in (1, 2):
+        assert sorted(int(i) for i, x in zip(items, parts) if x == pt) == sorted(split)
+    ew = np.where(parts == 0, weights[items], np.where(parts == 1, weights[items] // 2,
+                                                        weights[items] - weights[items] // 2))
+    assert np.all(np.diff(ew) <= 0)
+    for i in split:
+        assert 0 <= mids[i] <= nkb
+    refs = [O.bsa(_np(q[p:]), _np(k[128:p]), _np(v[128:p]), p, 128, mask, 0, False),
+            O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True),
+            O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, np.broadcast_to(row, (hq, nqb, p // 128)), 0, False)]
+    for (go, gl), (ro, rl) in zip(outs, refs):
+        PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
+
+
+def test_segments_split_items():
+    """Rows of ~40 kept tiles on a small grid: every such item is split in two at its median kept block,
+    the halves run as separate entries and are merged by LSE; out and LSE match the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, L, p = 4, 2, 128, 8192, 7680
+    q = _rand((L, hq, d), torch.bfloat16, 86)
+    k = _rand((L, hkv, d), torch.bfloat16, 87)
+    v = _rand((L, hkv, d), torch.bfloat16, 88)
+    qd, kd = q.to(DEV), k.to(DEV)
+    packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
+    B.bsa_pack_v(v.to(DEV), packed, 0)
+    rng = np.random.default_rng(11)
+    nqb, nkb = (L - p) // 128, L // 128
+    mask = (rng.random((hq, nqb, nkb)) < 0.7).astype(np.uint8)
+    mask[:, :, 0] = 1
+    md = torch.from_numpy(mask).to(DEV)
+    outs = [(torch.empty(L - p, hq, d, dtype=torch.bfloat16, device=DEV),
+             torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(2)]
+    segs = [dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=md, causal=False, out=outs[0][0],
+                 lse=outs[0][1]),
+            dict(k=kd[p:], kv_start=p, v_token_offset=p, block_mask=md, causal=True, out=outs[1][0], lse=outs[1][1])]
+    ws = B.workspace(B.bsa_prefill_segments_workspace_size(L - p, hq, d, 2), DEV)
+    B.bsa_prefill_segments(qd[p:], packed, p, segs, ws=ws)
+    torch.cuda.synchronize()
+    ctl = ws[:12].cpu().numpy().view(np.int32)
+    hist_rows = mask[:, :, :p // 128].sum(axis=2)
+    assert (hist_rows >= 32).all()
+    assert ctl[2] == hq * nqb, f"expected every history item split, got {ctl[2]}"
+    refs = [O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, mask, 0, False),
+            O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True)]
+    for (go, gl), (ro, rl) in zip(outs, refs):
+        PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
