@@ -127,13 +127,17 @@ def count_flops(run):
     return launches, est, sel / max(tot, 1), split
 
 
-def cpu_baseline(name, groups):
-    """Time the oracle on `groups` kv-head groups of the workload (all chunks)."""
+def cpu_baseline(name, groups, w):
+    """Time the oracle on `groups` kv-head groups of the workload.
+
+    Every chunk is timed when there are at most 8; otherwise chunks {first,
+    middle, last} are timed and the per-chunk time, linear in the history
+    length p (estimate and attention both scale with p + C), is fitted by least
+    squares and summed over all chunks.
+    """
     import numpy as np
-    import torch
     from block_sparse_attention_xattn_amd import synthetic
     from oracle import xattn_oracle as O
-    w = synthetic.WORKLOADS[name]
     q, k, v = synthetic.workload_inputs(name)
     g = w["hq"] // w["hkv"]
     hs = list(range(groups * g))
@@ -144,15 +148,29 @@ def cpu_baseline(name, groups):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
-    t0 = time.perf_counter()
-    O.chunked_prefill(qs, ks, vs, w["chunk"], w["stride"], w["threshold"])
-    dt = time.perf_counter() - t0
+    c = w["chunk"]
+    starts = [w["q_start_pos"]] if "q_start_pos" in w else list(range(0, w["L"], c))
+    sample = starts if len(starts) <= 8 else [starts[0], starts[len(starts) // 2], starts[-1]]
+    times = []
+    for p in sample:
+        t0 = time.perf_counter()
+        O.chunk_prefill(qs[p:p + c], ks, vs, p, w["stride"], w["threshold"])
+        times.append(time.perf_counter() - t0)
+    if len(sample) == len(starts):
+        total = sum(times)
+        how = f"all {len(starts)} chunk(s) timed"
+    else:
+        b1, b0 = np.polyfit(np.array(sample, dtype=np.float64), np.array(times), 1)
+        total = float(sum(b0 + b1 * p for p in starts))
+        how = (f"chunks at p = {sample} timed ({sum(times):.1f} s), per-chunk time fitted linearly in p and summed "
+               f"over all {len(starts)} chunks")
     frac = groups / w["hkv"]
-    value = w["L"] * frac / dt
+    value = len(starts) * c * frac / total
     return {"value": round(value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 numpy oracle, all {w['L'] // w['chunk']} chunks of the {w['L']}-token layer for "
-                      f"{groups} of {w['hkv']} kv-head groups ({len(hs)} of {w['hq']} query heads); "
-                      f"tokens/s scaled by the head fraction (heads are independent); {dt:.1f} s of CPU time"}
+            "sample": f"float64 numpy oracle (chunk_prefill: estimate, selection, sparse history and in-chunk "
+                      f"attention, merge) for {groups} of {w['hkv']} kv-head groups ({len(hs)} of {w['hq']} query "
+                      f"heads); {how}; tokens/s scaled by the head fraction (heads are independent); "
+                      f"{sum(times):.1f} s of CPU time"}
 
 
 def main():
@@ -181,7 +199,7 @@ def main():
     w["threshold"] = a.threshold if a.threshold is not None else w.get("threshold", 0.9)
     out = measure(a, w, q, k, v)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups)
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups, w)
     print(json.dumps(out))
 
 
