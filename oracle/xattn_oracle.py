@@ -23,7 +23,9 @@ Sources (the pages this follows; each function names its passage):
   "Online Softmax Merge - Triton Fused Kernel" (merge formula).
 * "Task plan" -- the nano-vllm ``task_plan.md`` page, section
   "select_blocks 设计" (OR of eight 128-token blocks into one 1024-token
-  cache block).
+  cache block), "Metadata 存储策略" (scheme A: keep K[::stride] of each
+  offloaded block) and "Phase 3: select_blocks 实现" (estimate the chunk
+  against the downsampled history with stride 1).
 
 Readings where the pages are open (each is restated where it is used):
 
@@ -40,6 +42,9 @@ Readings where the pages are open (each is restated where it is used):
   stride-1 reduction and the invariants the tests check.
 * LSE is natural-log, laid out [heads, q_len]; an empty key set gives out 0
   and lse -inf; merging with an lse of -inf returns the other input.
+* Estimate against the downsampled history: every history key precedes the
+  chunk, so no causal limit applies, and the chunk's diagonal block lies past
+  the history keys, so block 0 is the only forced block.
 
 All arrays are numpy float64 unless stated; token-major layouts
 ``[tokens, heads, head_dim]`` as in the pages' varlen tensors.
@@ -497,3 +502,64 @@ def density(mask, q_start_pos: int, block: int = 128) -> float:
     cur = q_start_pos // block
     causal = np.arange(nKB)[None, :] <= (cur + np.arange(nQB))[:, None]
     return float((mask & causal[None]).sum()) / float(causal.sum() * H)
+
+
+# ---------------------------------------------------------------------------
+# Next step: the estimate against downsampled history keys (metadata of
+# offloaded K)
+# ---------------------------------------------------------------------------
+
+def downsample_keys(k, stride: int) -> np.ndarray:
+    """Task plan, "Metadata 存储策略", scheme A (``on_prefill_offload``): of
+    each offloaded block keep every stride-th key token, K[::stride].
+
+    k: [n, Hkv, d] -> [ceil(n / stride), Hkv, d].
+    """
+    return np.asarray(k)[::stride]
+
+
+def estimate_history_downsampled(q, k_ds, stride: int, threshold: float, block: int = 128,
+                                 rule: str = "greedy"):
+    """Block scores and mask of a query chunk against the downsampled history.
+
+    Task plan, "Phase 3: select_blocks 实现": the chunked estimate is run with
+    stride 1 on (Q, K[::stride]) with block size block / stride, so a block of
+    the downsampled key axis stands for one block-token block of the history
+    and the query axis is cut into blocks of block / stride tokens.  At
+    stride 1 the logits are q.k / sqrt(d) per (query token, downsampled key);
+    each row is normalised over all history keys (all precede the chunk) and
+    the probabilities are summed over (block/stride x block/stride) tiles.
+    Selection per row as ``select_row`` with block 0 the only forced block
+    (the chunk's diagonal block lies past the history keys).
+
+    q: [Lq, Hq, d]; k_ds: [n_ds, Hkv, d].
+    Returns (scores [Hq, Lq / b, n_ds / b], mask uint8 of the same shape), b = block / stride.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_ds = np.asarray(k_ds, dtype=np.float64)
+    Lq, Hq, d = q.shape
+    n_ds, Hkv, _ = k_ds.shape
+    b = block // stride
+    assert block % stride == 0 and Lq % b == 0 and n_ds % b == 0
+    g = Hq // Hkv
+    scores = []
+    for h in range(Hq):
+        z = q[:, h] @ k_ds[:, h // g].T / math.sqrt(d)
+        prob, _, _ = row_softmax_causal(z, np.ones_like(z, dtype=bool))
+        scores.append(block_sums(prob, b, 1))
+    scores = np.stack(scores)
+    mask = np.zeros(scores.shape, dtype=np.uint8)
+    for h in range(Hq):
+        for qb in range(scores.shape[1]):
+            mask[h, qb] = select_row(scores[h, qb], [0], threshold, rule)
+    return scores, mask
+
+
+def history_cache_blocks_downsampled(mask, n_cache_blocks: int, sub_blocks: int = 8) -> np.ndarray:
+    """Task plan, "Phase 3: select_blocks 实现" steps 5-6: OR of the mask over
+    heads and query blocks, then a cache block of sub_blocks 128-token blocks
+    is kept when any of them is (no forced first / last block in this sketch).
+
+    mask: [Hq, nQB, n_blocks] -> keep uint8 [n_cache_blocks].
+    """
+    return mask_to_cache_blocks(mask, 0, n_cache_blocks, sub_blocks, force_first_last=False)[1]
