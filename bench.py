@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-groups", type=int, default=1, help="kv-head groups timed for the CPU baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain device copy of this many MiB")
     ap.add_argument("--sweep", action="store_true", help="every (stride, threshold) of the workload, one line each")
+    ap.add_argument("--estimator", choices=("full", "downsampled"), default="full",
+                    help="downsampled: cache blocks chosen from K[::stride] of the history (cache-block workloads)")
     return ap.parse_args()
 
 
@@ -93,7 +95,24 @@ def count_flops(run):
     split = {"history": 0.0, "in_chunk": 0.0, "useful": 0.0}
     est = 0.0
     sel = tot = 0
+    ds = getattr(run, "estimator", "full") == "downsampled"
     for b in run.bufs:
+        if ds:
+            # estimate against K[::S] of the history; history attention over the kept cache blocks
+            hq, nqb = run.hq, min(run.chunk, run.L - b.p) // blk
+            parts = [("in_chunk", per_tile * hq * nqb * (nqb + 1) / 2)]
+            if b.p > 0:
+                kept = int(b.keep_any_blocks.cpu().numpy().astype(bool).sum())
+                parts.insert(0, ("history", per_tile * kept * hq * nqb))
+                est += 2.0 * d * (nqb * blk) * (b.p // S) * hq
+                sel += kept * hq * nqb
+            sel += hq * nqb * (nqb + 1) // 2
+            tot += hq * nqb * (b.p // blk) + hq * nqb * (nqb + 1) // 2
+            for kind, f in parts:
+                split[kind] += f
+            split["useful"] += sum(f for _, f in parts) - per_tile * hq * nqb * (1.0 - (blk + 1) / (2.0 * blk))
+            launches.append(sum(f for _, f in parts))
+            continue
         m = b.mask.cpu().numpy().astype(bool)
         hq, nqb, nkb = m.shape
         cur = b.p // blk
@@ -211,7 +230,7 @@ def measure(a, w, q, k, v):
     if "q_start_pos" in w:
         starts = [w["q_start_pos"]]
     run = ChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
-                         chunk_starts=starts, cache_block=w.get("cache_block"))
+                         chunk_starts=starts, cache_block=w.get("cache_block"), estimator=a.estimator)
     run.pack_history()
     torch.cuda.synchronize()
     for _ in range(a.warmup):
@@ -332,7 +351,7 @@ def measure(a, w, q, k, v):
         "data": "synthetic",
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
                    "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
-                   "block": 128, "chunks_timed": len(run.starts)},
+                   "block": 128, "chunks_timed": len(run.starts), "estimator": a.estimator},
         "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
@@ -349,7 +368,32 @@ def measure(a, w, q, k, v):
         "bsa_useful_tflops": round(split["useful"] * a.steps / (sum(bsa_durs) * 1e-3) / 1e12, 1),
         **hbm,
     }
+    if a.estimator == "downsampled":
+        out["vs_full_estimator"] = compare_estimators(run, q, k, v, w, starts)
     return out
+
+
+def compare_estimators(run, q, k, v, w, starts):
+    """Cache blocks kept by the downsampled estimate against those of the full estimate (untimed)."""
+    import torch
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
+    full = ChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
+                          chunk_starts=starts, cache_block=w.get("cache_block"))
+    full.run()
+    torch.cuda.synchronize()
+    both = n_full = n_ds = n_all = 0
+    for bd, bf in zip(run.bufs, full.bufs):
+        if bd.keep_any is None:
+            continue
+        kd = bd.keep_any.cpu().numpy().astype(bool)
+        kf = bf.keep_any.cpu().numpy().astype(bool)
+        both += int((kd & kf).sum())
+        n_full += int(kf.sum())
+        n_ds += int(kd.sum())
+        n_all += kd.size
+    diff = (run.out.float() - full.out.float()).abs().max().item()
+    return {"cache_blocks": n_all, "kept_full": n_full, "kept_downsampled": n_ds,
+            "recall_of_full": round(both / max(n_full, 1), 4), "out_max_abs_diff": round(diff, 4)}
 
 
 if __name__ == "__main__":

@@ -71,6 +71,13 @@ def _declare(lib):
                                          ctypes.POINTER(Segment), I32, I32, F, ctypes.c_int, P, SZ, P]
     lib.bsa_prefill_segments_workspace_size.restype = SZ
     lib.bsa_prefill_segments_workspace_size.argtypes = [I64, I32, I32, I32]
+    lib.xattn_downsample_keys.restype = ctypes.c_int
+    lib.xattn_downsample_keys.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I32, I32, P, I64, I64, P]
+    lib.xattn_estimate_history_ds_workspace_size.restype = SZ
+    lib.xattn_estimate_history_ds_workspace_size.argtypes = [I64, I64, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.xattn_estimate_history_ds.restype = ctypes.c_int
+    lib.xattn_estimate_history_ds.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32, I32,
+                                              I32, F, P, P, P, SZ, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -289,6 +296,46 @@ def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax
                                       q_len, hq, packed.hkv, d, q_start_pos, arr, len(segments), block,
                                       float(softmax_scale), odt, _ptr(ws), ws.numel(), _stream(stream)))
     return keep
+
+
+def xattn_downsample_keys(k, stride: int, k_ds, ds_offset: int = 0, stream=None):
+    """Rows ds_offset .. ds_offset + len(k)/stride - 1 of k_ds [capacity, Hkv, d] become K[::stride]."""
+    _qkv_check(k, "k")
+    n, hkv, d = k.shape
+    if not k_ds.is_cuda or not k_ds.is_contiguous() or k_ds.dim() != 3 or k_ds.dtype != k.dtype:
+        raise XattnError(XA_EINVAL, "k_ds must be a contiguous GPU tensor [capacity, Hkv, d] of k's dtype")
+    _check(lib().xattn_downsample_keys(_ptr(k), k.stride(0), k.stride(1), _dtype_code(k), n, hkv, d, stride,
+                                       _ptr(k_ds), k_ds.shape[0], ds_offset, _stream(stream)))
+    return k_ds
+
+
+def xattn_estimate_history_ds_workspace_size(q_len, n_ds, num_q_heads, num_kv_heads, head_dim, stride, block=128,
+                                             dtype=XA_BF16) -> int:
+    return int(lib().xattn_estimate_history_ds_workspace_size(q_len, n_ds, num_q_heads, num_kv_heads, head_dim,
+                                                              stride, block, dtype))
+
+
+def xattn_estimate_history_ds(q, k_ds, stride: int, threshold: float, block: int = 128, block_scores=None,
+                              block_mask=None, ws=None, stream=None):
+    """Estimate of a query chunk against downsampled history keys (see xattn.h).  Returns (scores, mask)."""
+    _qkv_check(q, "q")
+    _qkv_check(k_ds, "k_ds")
+    q_len, hq, d = q.shape
+    n_ds, hkv, _ = k_ds.shape
+    b = block // stride
+    dt = _dtype_code(q)
+    if block_scores is None:
+        block_scores = torch.empty(hq, q_len // b, n_ds // b, dtype=torch.float32, device=q.device)
+    if block_mask is None:
+        block_mask = torch.empty(hq, q_len // b, n_ds // b, dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = workspace(xattn_estimate_history_ds_workspace_size(q_len, n_ds, hq, hkv, d, stride, block, dt),
+                       q.device)
+    _check(lib().xattn_estimate_history_ds(_ptr(q), q.stride(0), q.stride(1), _ptr(k_ds), k_ds.stride(0),
+                                           k_ds.stride(1), dt, q_len, n_ds, hq, hkv, d, stride, block,
+                                           float(threshold), _ptr(block_scores), _ptr(block_mask), _ptr(ws),
+                                           ws.numel(), _stream(stream)))
+    return block_scores, block_mask
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -108,44 +108,26 @@ extern "C" size_t xattn_estimate_workspace_size(int64_t q_len, int64_t k_len, in
   return est_layout(q_len, k_len, num_q_heads, num_kv_heads, head_dim, stride, block, dtype).total;
 }
 
-extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
-                                      int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len,
-                                      int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int32_t stride,
-                                      int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
-                                      void* workspace, size_t ws_bytes, xa_stream_t stream) {
-  const char* fn = "xattn_estimate";
-  xa_status_t st;
-  if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
-  if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
-  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
-  if (stride != 2 && stride != 4 && stride != 8 && stride != 16)
-    return fail(XA_EUNSUPPORTED, "%s: stride %d not in {2, 4, 8, 16}", fn, stride);
-  if (q_len <= 0 || q_len % block != 0) return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of %d", fn, (long long)q_len, block);
-  if (q_start < 0 || q_start % block != 0) return fail(XA_EINVAL, "%s: q_start_pos %lld must be a non-negative multiple of %d", fn, (long long)q_start, block);
-  if (k_len != q_start + q_len) return fail(XA_EINVAL, "%s: k_len %lld != q_start_pos + q_len = %lld", fn, (long long)k_len, (long long)(q_start + q_len));
-  if (k_len / block > 8192) return fail(XA_EUNSUPPORTED, "%s: k_len / block = %lld exceeds 8192 key blocks", fn, (long long)(k_len / block));
-  if (!(threshold >= 0.f) || isnan(threshold)) return fail(XA_EINVAL, "%s: threshold must be >= 0", fn);
-  if ((st = check_tensor(fn, "q", q, q_tok, q_head, q_len, hq, d, dtype)) != XA_OK) return st;
-  if ((st = check_tensor(fn, "k", k, k_tok, k_head, k_len, hkv, d, dtype)) != XA_OK) return st;
-  if (!block_scores || !block_mask) return fail(XA_EINVAL, "%s: block_scores and block_mask are required", fn);
-  const EstLayout L = est_layout(q_len, k_len, hq, hkv, d, stride, block, dtype);
-  if (!workspace || ws_bytes < L.total || (uintptr_t)workspace % 256 != 0)
-    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, L.total,
-                ws_bytes);
-  const int64_t R = q_len / stride, N = k_len / stride, nkb = k_len / block;
-  if ((int64_t)hq * nkb * R > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+namespace {
+// Estimate GEMM (reshaped by stride S, b rows per query block) + selection.
+// q_start_eff fixes the causal limit of reshaped column c for row r:
+// c <= q_start_eff / S + r.  hist_only: all key blocks visible, block 0 the
+// only forced block.
+xa_status_t estimate_core(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                          int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len, int32_t hq, int32_t hkv,
+                          int32_t d, int32_t stride, int32_t b, int64_t q_start_eff, int64_t n_qb, int64_t cur,
+                          bool hist_only, float threshold, float* block_scores, uint8_t* block_mask, char* ws,
+                          const EstLayout& L, hipStream_t s) {
+  const int64_t R = q_len / stride, N = k_len / stride, nkb = N / b;
   EstParams p{};
   p.q_len = q_len;
   p.k_len = k_len;
-  p.q_start = q_start;
+  p.q_start = q_start_eff;
   p.hq = hq;
   p.hkv = hkv;
   p.group = hq / hkv;
   p.S = stride;
-  p.b = block / stride;
+  p.b = b;
   p.R = (int)R;
   p.N = (int)N;
   p.nkb = (int)nkb;
@@ -193,14 +175,116 @@ extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_he
   while (sp.npow_cap < p.nkb) sp.npow_cap <<= 1;
   sp.b = p.b;
   sp.hq = hq;
-  sp.n_qb = (int)(q_len / block);
-  sp.cur = q_start / block;
+  sp.n_qb = (int)n_qb;
+  sp.hist_only = hist_only ? 1 : 0;
+  sp.cur = cur;
   sp.threshold = threshold;
   sp.scores = block_scores;
   sp.mask = block_mask;
   if ((e = launch_est_select(sp, s)) != hipSuccess)
     return fail(XA_EHIP, "%s: selection launch failed: %s", fn, hipGetErrorString(e));
   return XA_OK;
+}
+}  // namespace
+
+extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                                      int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len,
+                                      int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int32_t stride,
+                                      int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
+                                      void* workspace, size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "xattn_estimate";
+  xa_status_t st;
+  if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
+  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (stride != 2 && stride != 4 && stride != 8 && stride != 16)
+    return fail(XA_EUNSUPPORTED, "%s: stride %d not in {2, 4, 8, 16}", fn, stride);
+  if (q_len <= 0 || q_len % block != 0) return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of %d", fn, (long long)q_len, block);
+  if (q_start < 0 || q_start % block != 0) return fail(XA_EINVAL, "%s: q_start_pos %lld must be a non-negative multiple of %d", fn, (long long)q_start, block);
+  if (k_len != q_start + q_len) return fail(XA_EINVAL, "%s: k_len %lld != q_start_pos + q_len = %lld", fn, (long long)k_len, (long long)(q_start + q_len));
+  if (k_len / block > 8192) return fail(XA_EUNSUPPORTED, "%s: k_len / block = %lld exceeds 8192 key blocks", fn, (long long)(k_len / block));
+  if (!(threshold >= 0.f) || isnan(threshold)) return fail(XA_EINVAL, "%s: threshold must be >= 0", fn);
+  if ((st = check_tensor(fn, "q", q, q_tok, q_head, q_len, hq, d, dtype)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "k", k, k_tok, k_head, k_len, hkv, d, dtype)) != XA_OK) return st;
+  if (!block_scores || !block_mask) return fail(XA_EINVAL, "%s: block_scores and block_mask are required", fn);
+  const EstLayout L = est_layout(q_len, k_len, hq, hkv, d, stride, block, dtype);
+  if (!workspace || ws_bytes < L.total || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, L.total,
+                ws_bytes);
+  const int64_t R = q_len / stride, nkb = k_len / block;
+  if ((int64_t)hq * nkb * R > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
+  return estimate_core(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, k_len, hq, hkv, d, stride,
+                       block / stride, q_start, q_len / block, q_start / block, false, threshold, block_scores,
+                       block_mask, static_cast<char*>(workspace), L, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Downsampled history keys and the estimate against them
+// ---------------------------------------------------------------------------
+extern "C" xa_status_t xattn_downsample_keys(const void* k, int64_t k_tok, int64_t k_head, xa_dtype_t dtype,
+                                             int64_t n_tokens, int32_t hkv, int32_t d, int32_t stride, void* k_ds,
+                                             int64_t ds_capacity, int64_t ds_offset, xa_stream_t stream) {
+  const char* fn = "xattn_downsample_keys";
+  xa_status_t st;
+  if ((st = check_heads(fn, hkv, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
+  if (stride < 1) return fail(XA_EINVAL, "%s: stride must be positive (got %d)", fn, stride);
+  if (n_tokens <= 0 || n_tokens % stride != 0)
+    return fail(XA_EINVAL, "%s: n_tokens %lld must be a positive multiple of the stride %d", fn, (long long)n_tokens,
+                stride);
+  const int64_t n_out = n_tokens / stride;
+  if (ds_offset < 0 || ds_capacity <= 0 || ds_offset + n_out > ds_capacity)
+    return fail(XA_EINVAL, "%s: rows [%lld, %lld) outside the capacity %lld", fn, (long long)ds_offset,
+                (long long)(ds_offset + n_out), (long long)ds_capacity);
+  if ((st = check_tensor(fn, "k", k, k_tok, k_head, n_tokens, hkv, d, dtype)) != XA_OK) return st;
+  if (!k_ds || (uintptr_t)k_ds % 16 != 0) return fail(XA_EINVAL, "%s: k_ds must be 16-byte aligned", fn);
+  const hipError_t e = launch_downsample_keys(k, dtype, k_tok, k_head, n_out, hkv, d, stride, k_ds, ds_offset,
+                                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return XA_OK;
+}
+
+extern "C" size_t xattn_estimate_history_ds_workspace_size(int64_t q_len, int64_t n_ds, int32_t num_q_heads,
+                                                           int32_t num_kv_heads, int32_t head_dim, int32_t stride,
+                                                           int32_t block, xa_dtype_t dtype) {
+  if (q_len <= 0 || n_ds <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || stride <= 0 ||
+      block <= 0 || block % stride != 0)
+    return 0;
+  return est_layout(q_len, n_ds, num_q_heads, num_kv_heads, head_dim, 1, block / stride, dtype).total;
+}
+
+extern "C" xa_status_t xattn_estimate_history_ds(const void* q, int64_t q_tok, int64_t q_head, const void* k_ds,
+                                                 int64_t kds_tok, int64_t kds_head, xa_dtype_t dtype, int64_t q_len,
+                                                 int64_t n_ds, int32_t hq, int32_t hkv, int32_t d, int32_t stride,
+                                                 int32_t block, float threshold, float* block_scores,
+                                                 uint8_t* block_mask, void* workspace, size_t ws_bytes,
+                                                 xa_stream_t stream) {
+  const char* fn = "xattn_estimate_history_ds";
+  xa_status_t st;
+  if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
+  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (stride != 2 && stride != 4 && stride != 8 && stride != 16)
+    return fail(XA_EUNSUPPORTED, "%s: stride %d not in {2, 4, 8, 16}", fn, stride);
+  const int b = block / stride;
+  if (q_len <= 0 || q_len % b != 0)
+    return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of block / stride = %d", fn, (long long)q_len, b);
+  if (n_ds <= 0 || n_ds % b != 0)
+    return fail(XA_EINVAL, "%s: n_ds %lld must be a positive multiple of block / stride = %d", fn, (long long)n_ds, b);
+  if (n_ds / b > 8192) return fail(XA_EUNSUPPORTED, "%s: n_ds / (block / stride) exceeds 8192 key blocks", fn);
+  if (!(threshold >= 0.f) || isnan(threshold)) return fail(XA_EINVAL, "%s: threshold must be >= 0", fn);
+  if ((st = check_tensor(fn, "q", q, q_tok, q_head, q_len, hq, d, dtype)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "k_ds", k_ds, kds_tok, kds_head, n_ds, hkv, d, dtype)) != XA_OK) return st;
+  if (!block_scores || !block_mask) return fail(XA_EINVAL, "%s: block_scores and block_mask are required", fn);
+  const EstLayout L = est_layout(q_len, n_ds, hq, hkv, d, 1, b, dtype);
+  if (!workspace || ws_bytes < L.total || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, L.total,
+                ws_bytes);
+  if ((int64_t)hq * (n_ds / b) * q_len > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
+  // stride 1 over the downsampled keys; the causal limit c <= n_ds + r never binds (history only)
+  return estimate_core(fn, q, q_tok, q_head, k_ds, kds_tok, kds_head, dtype, q_len, n_ds, hq, hkv, d, 1, b, n_ds,
+                       q_len / b, 0, true, threshold, block_scores, block_mask, static_cast<char*>(workspace), L,
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -317,8 +317,9 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
   const int h = blockIdx.x / P.n_qb;
   const int qb = blockIdx.x % P.n_qb;
   constexpr int b = B;
-  const int64_t diag = P.cur + qb;  // always-kept diagonal block
-  const int nvis = (int)diag + 1;   // key blocks 0..diag
+  // always-kept diagonal block; key blocks 0..diag visible (history only: all, no diagonal)
+  const int64_t diag = P.hist_only ? -1 : P.cur + qb;
+  const int nvis = P.hist_only ? P.nkb : (int)diag + 1;
   const float* base = P.lse_part + (int64_t)h * P.nkb * P.R + (int64_t)qb * b;
 
   // pass 1: per-row normaliser over key blocks (log2 units)
@@ -404,7 +405,8 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
     __syncthreads();
   }
 
-  const int n_other = nvis - 2 > 0 ? nvis - 2 : 0;  // sortable blocks (0 and diag excluded)
+  const int n_forced = diag > 0 ? 2 : 1;  // block 0, and the diagonal when it is another block
+  const int n_other = nvis - n_forced > 0 ? nvis - n_forced : 0;  // sortable blocks
   if (!all && n_other > 0) {
     // bitonic sort, ascending key = descending score, then ascending index
     for (int k = 2; k <= npow; k <<= 1) {
@@ -485,6 +487,39 @@ template hipError_t launch_est_gemm<64, false>(const EstParams&, hipStream_t);
 template hipError_t launch_est_gemm<64, true>(const EstParams&, hipStream_t);
 template hipError_t launch_est_gemm<128, false>(const EstParams&, hipStream_t);
 template hipError_t launch_est_gemm<128, true>(const EstParams&, hipStream_t);
+
+// K[::stride] of n_out * stride key rows -> dense rows out_off .. out_off + n_out - 1
+// of a [capacity][hkv][d] buffer; one 16-byte piece per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void downsample_keys_kernel(const T* __restrict__ k, int64_t k_tok, int64_t k_head,
+                                                              int64_t n_out, int hkv, int d, int stride,
+                                                              T* __restrict__ out, int64_t out_off) {
+  constexpr int E = 16 / sizeof(T);  // elements per piece
+  const int pieces = d / E;
+  const int64_t total = n_out * hkv * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % pieces);
+    const int h = (int)((i / pieces) % hkv);
+    const int64_t j = i / ((int64_t)pieces * hkv);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(k + j * stride * k_tok + (int64_t)h * k_head + c * E);
+    *reinterpret_cast<u32x4*>(out + ((out_off + j) * hkv + h) * d + c * E) = v;
+  }
+}
+
+hipError_t launch_downsample_keys(const void* k, xa_dtype_t dt, int64_t k_tok, int64_t k_head, int64_t n_out, int hkv,
+                                  int d, int stride, void* out, int64_t out_off, hipStream_t s) {
+  const int64_t pieces = n_out * hkv * (d * (dt == XA_BF16 ? 2 : 4) / 16);
+  int64_t blocks = (pieces + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (dt == XA_BF16)
+    hipLaunchKernelGGL(downsample_keys_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16*)k, k_tok,
+                       k_head, n_out, hkv, d, stride, (bf16*)out, out_off);
+  else
+    hipLaunchKernelGGL(downsample_keys_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)k,
+                       k_tok, k_head, n_out, hkv, d, stride, (float*)out, out_off);
+  return hipGetLastError();
+}
 
 hipError_t launch_est_select(const SelParams& p, hipStream_t s) {
   const dim3 grid(p.hq * p.n_qb);

@@ -45,8 +45,9 @@ struct EstParams {
 struct SelParams {
   const float* lse_part;
   int R, nkb, b, hq, n_qb;
-  int npow_cap;  // smallest power of two >= nkb (sort buffer length)
-  int64_t cur;   // key blocks before the chunk (q_start / 128)
+  int npow_cap;   // smallest power of two >= nkb (sort buffer length)
+  int hist_only;  // 1: keys are history only (all visible, block 0 the only forced block)
+  int64_t cur;    // key blocks before the chunk (q_start / 128)
   float threshold;
   float* scores;  // [hq][n_qb][nkb]
   uint8_t* mask;  // [hq][n_qb][nkb]
@@ -120,5 +121,7 @@ hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, in
 template <int D, bool SPLIT>
 hipError_t launch_est_gemm(const EstParams& p, hipStream_t s);
 hipError_t launch_est_select(const SelParams& p, hipStream_t s);
+hipError_t launch_downsample_keys(const void* k, xa_dtype_t dt, int64_t k_tok, int64_t k_head, int64_t n_out, int hkv,
+                                  int d, int stride, void* out, int64_t out_off, hipStream_t s);
 
 }  // namespace xa

@@ -9,7 +9,11 @@ compute_chunked_prefill: for the query chunk at global position p,
 The cache-block variant first reduces the history part of the mask to
 1024-token cache blocks (union over heads and query blocks, first and last
 forced) and attends every 128-token block of the kept cache blocks, with
-dense causal attention inside the chunk.
+dense causal attention inside the chunk.  With estimator="downsampled" (task
+plan page, "Metadata 存储策略" and "Phase 3: select_blocks 实现") the cache
+blocks are chosen instead from an estimate of the chunk against K[::stride]
+of the history, which each chunk appends for its own keys; the full K is
+then not read by the estimate.
 
 V is kept packed once per layer in the attention kernel's layout: each chunk
 packs its own V rows when it starts (bsa_pack_v), and both attention calls
@@ -50,12 +54,17 @@ class ChunkedPrefill:
     """
 
     def __init__(self, q, k, v, chunk: int, stride: int, threshold: float, block: int = 128,
-                 chunk_starts=None, cache_block: int | None = None, out_dtype=None):
+                 chunk_starts=None, cache_block: int | None = None, out_dtype=None, estimator: str = "full"):
         self.q, self.k, self.v = q, k, v
         self.L, self.hq, self.d = q.shape
         self.hkv = k.shape[1]
         self.chunk, self.stride, self.threshold, self.block = chunk, stride, threshold, block
         self.cache_block = cache_block
+        if estimator not in ("full", "downsampled"):
+            raise ValueError("estimator must be 'full' or 'downsampled'")
+        if estimator == "downsampled" and not cache_block:
+            raise ValueError("the downsampled estimator selects cache blocks: pass cache_block")
+        self.estimator = estimator
         dev = q.device
         self.out_dtype = q.dtype if out_dtype is None else out_dtype
         self.starts = list(range(0, self.L, chunk)) if chunk_starts is None else list(chunk_starts)
@@ -65,6 +74,12 @@ class ChunkedPrefill:
                                                      self.hq, self.hkv, self.d, stride, block, dt)
                      for p in self.starts)
         bsa_ws = B.bsa_prefill_packed_workspace_size(chunk, max_k, self.hq, self.hkv, self.d, dt)
+        if estimator == "downsampled":
+            bds = block // stride
+            est_ws = max([B.xattn_estimate_history_ds_workspace_size(min(chunk, self.L - p), p // stride, self.hq,
+                                                                      self.hkv, self.d, stride, block, dt)
+                          for p in self.starts if p > 0] or [0])
+            self.k_ds = torch.empty(self.L // stride, self.hkv, self.d, dtype=k.dtype, device=dev)
         self.est_ws = B.workspace(est_ws, dev)
         self.bsa_ws = B.workspace(bsa_ws, dev) if bsa_ws > 0 else None
         self.seg_ws = B.workspace(B.bsa_prefill_segments_workspace_size(chunk, self.hq, self.d, 2), dev)
@@ -76,16 +91,21 @@ class ChunkedPrefill:
             nqb, nkb = c // block, (p + c) // block
             hist = p > 0
             kb = None
+            if estimator == "downsampled":
+                # scores / mask over (query blocks of block/stride tokens, history blocks)
+                shp = (self.hq, c // (block // stride), max(p // block, 1))
+            else:
+                shp = (self.hq, nqb, nkb)
             if hist and cache_block:
                 sub = cache_block // block
                 ncb = p // cache_block
-                kb = dict(keep_per_head=torch.empty(self.hq, nqb, ncb, dtype=torch.uint8, device=dev),
+                kb = dict(keep_per_head=torch.empty(self.hq, shp[1], ncb, dtype=torch.uint8, device=dev),
                           keep_any=torch.empty(ncb, dtype=torch.uint8, device=dev),
                           keep_any_blocks=torch.empty(ncb * sub, dtype=torch.uint8, device=dev))
             self.bufs.append(ChunkBuffers(
                 p=p,
-                scores=torch.empty(self.hq, nqb, nkb, dtype=torch.float32, device=dev),
-                mask=torch.empty(self.hq, nqb, nkb, dtype=torch.uint8, device=dev),
+                scores=torch.empty(*shp, dtype=torch.float32, device=dev),
+                mask=torch.empty(*shp, dtype=torch.uint8, device=dev),
                 o_hist=torch.empty(c, self.hq, self.d, dtype=self.out_dtype, device=dev) if hist else None,
                 l_hist=torch.empty(self.hq, c, dtype=torch.float32, device=dev) if hist else None,
                 o_cur=torch.empty(c, self.hq, self.d, dtype=self.out_dtype, device=dev) if hist else self.out[p:p + c],
@@ -94,18 +114,31 @@ class ChunkedPrefill:
                 **(kb or {})))
 
     # -- the calls of one chunk --------------------------------------------------
+    def _len(self, b: ChunkBuffers) -> int:
+        return min(self.chunk, self.L - b.p)
+
     def pack_history(self):
-        """Pack V rows before the first selected chunk (produced by earlier chunks)."""
+        """Pack V rows (and K[::stride] for the downsampled estimator) before the first selected chunk."""
         p0 = self.starts[0]
         if p0 > 0:
             B.bsa_pack_v(self.v[:p0], self.packed, 0)
+            if self.estimator == "downsampled":
+                B.xattn_downsample_keys(self.k[:p0], self.stride, self.k_ds, 0)
 
     def pack(self, b: ChunkBuffers):
-        c = b.scores.shape[1] * self.block
+        c = self._len(b)
         B.bsa_pack_v(self.v[b.p:b.p + c], self.packed, b.p)
+        if self.estimator == "downsampled":
+            B.xattn_downsample_keys(self.k[b.p:b.p + c], self.stride, self.k_ds, b.p // self.stride)
 
     def estimate(self, b: ChunkBuffers):
-        c = b.scores.shape[1] * self.block
+        c = self._len(b)
+        if self.estimator == "downsampled":
+            if b.p > 0:
+                B.xattn_estimate_history_ds(self.q[b.p:b.p + c], self.k_ds[:b.p // self.stride], self.stride,
+                                            self.threshold, self.block, block_scores=b.scores, block_mask=b.mask,
+                                            ws=self.est_ws)
+            return
         B.xattn_estimate(self.q[b.p:b.p + c], self.k[:b.p + c], b.p, self.stride, self.threshold, self.block,
                          block_scores=b.scores, block_mask=b.mask, ws=self.est_ws)
 
@@ -113,14 +146,15 @@ class ChunkedPrefill:
         if b.keep_any is None:
             return
         ncb = b.keep_any.shape[0]
-        B.xattn_mask_to_cache_blocks(b.mask, 0, ncb, self.cache_block // self.block, True,
+        # the downsampled estimate's sketch keeps the union only (no forced first / last cache block)
+        B.xattn_mask_to_cache_blocks(b.mask, 0, ncb, self.cache_block // self.block, self.estimator == "full",
                                      keep_per_head=b.keep_per_head, keep_any=b.keep_any,
                                      keep_any_blocks=b.keep_any_blocks)
 
     def attend(self, b: ChunkBuffers):
         """History (no causal rule) and the chunk's own keys (causal) in one segmented launch."""
         p = b.p
-        c = b.scores.shape[1] * self.block
+        c = self._len(b)
         qc = self.q[p:p + c]
         segs = []
         if p > 0:
@@ -145,7 +179,7 @@ class ChunkedPrefill:
     def merge(self, b: ChunkBuffers):
         if b.p == 0:
             return
-        c = b.scores.shape[1] * self.block
+        c = self._len(b)
         B.attn_merge(b.o_hist, b.l_hist, b.o_cur, b.l_cur, o_out=self.out[b.p:b.p + c], lse_out=b.lse)
 
     def run_chunk(self, i: int):

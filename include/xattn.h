@@ -242,6 +242,50 @@ xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok_stride, int64_t q_
                                  void* workspace, size_t workspace_bytes, xa_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Estimate against downsampled history keys (metadata of offloaded K)
+ *
+ * Task plan page, "Metadata 存储策略" scheme A and "Phase 3: select_blocks
+ * 实现": every stride-th key token of each offloaded block is kept on the
+ * GPU, and a query chunk is estimated against that downsampled history with
+ * stride 1 and blocks of block / stride rows (one block of downsampled keys
+ * stands for one 128-token history block).  Per (query token, downsampled
+ * key) the logit is q.k / sqrt(head_dim); each row is normalised over all
+ * history keys (they all precede the chunk: no causal limit); block scores
+ * are the sums over (block/stride x block/stride) tiles; selection per row as
+ * xattn_estimate with block 0 the only forced block (the chunk's diagonal
+ * block lies past the history).  The union over heads and query blocks, by
+ * cache block, is xattn_mask_to_cache_blocks on the returned mask.
+ *
+ * xattn_downsample_keys: rows ds_offset .. ds_offset + n_tokens/stride - 1 of
+ *   k_ds ([ds_capacity][num_kv_heads][head_dim], dense, same dtype) become
+ *   key rows 0, stride, 2*stride, ... of k (strided as for xattn_estimate).
+ *   n_tokens must be a multiple of stride; k_ds 16-byte aligned.
+ * xattn_estimate_history_ds: q [q_len][num_q_heads][head_dim] (strided),
+ *   k_ds [n_ds][num_kv_heads][head_dim] (strided); q_len and n_ds multiples
+ *   of b = block / stride; block 128, stride in {2, 4, 8, 16}.
+ *   block_scores float [num_q_heads][q_len/b][n_ds/b], block_mask uint8 of the
+ *   same shape; workspace of xattn_estimate_history_ds_workspace_size bytes
+ *   (256-byte aligned): per (head, key block, query token) a log-sum-exp
+ *   partial, num_q_heads * (n_ds/b) * q_len floats (plus bf16 hi/lo planes of
+ *   Q and K for XA_F32).  Errors as for xattn_estimate.
+ * ------------------------------------------------------------------------ */
+xa_status_t xattn_downsample_keys(const void* k, int64_t k_tok_stride, int64_t k_head_stride, xa_dtype_t dtype,
+                                  int64_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t stride,
+                                  void* k_ds, int64_t ds_capacity, int64_t ds_offset, xa_stream_t stream);
+
+size_t xattn_estimate_history_ds_workspace_size(int64_t q_len, int64_t n_ds, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t stride,
+                                                int32_t block, xa_dtype_t dtype);
+
+xa_status_t xattn_estimate_history_ds(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                      const void* k_ds, int64_t k_tok_stride, int64_t k_head_stride,
+                                      xa_dtype_t dtype, int64_t q_len, int64_t n_ds,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t stride, int32_t block, float threshold,
+                                      float* block_scores, uint8_t* block_mask,
+                                      void* workspace, size_t workspace_bytes, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)
  *
  * nano-vllm CLAUDE.md, "Online Softmax Merge - Triton Fused Kernel":

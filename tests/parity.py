@@ -34,8 +34,11 @@ def check_scores(gpu, ref):
                            f"{float((err / (np.abs(ref) + 1e-30)).max()):.3e}")
 
 
-def mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block=128):
-    """Return (n_diff, n_exempt, list of unexplained (h, qb, kb)) for a mask comparison."""
+def mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block=128, hist_only=False):
+    """Return (n_diff, n_exempt, list of unexplained (h, qb, kb)) for a mask comparison.
+
+    hist_only: the keys are history only (every block visible, block 0 the only forced block).
+    """
     gpu_mask = np.asarray(gpu_mask).astype(bool)
     ref_mask = np.asarray(ref_mask).astype(bool)
     H, nQB, nKB = ref_mask.shape
@@ -47,10 +50,10 @@ def mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, bloc
     for h, qb, kb in diff:
         rows.setdefault((h, qb), []).append(kb)
     for (h, qb), kbs in rows.items():
-        diag = cur + qb
+        diag = nKB - 1 if hist_only else cur + qb
         a = ref_scores[h, qb, :diag + 1].astype(np.float64)
         total = a.sum()
-        forced = {0, diag}
+        forced = {0} if hist_only else {0, diag}
         others = sorted((i for i in range(diag + 1) if i not in forced), key=lambda i: (-a[i], i))
         run = sum(a[i] for i in forced)
         excl = {}
@@ -77,8 +80,9 @@ def mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, bloc
     return len(diff), n_exempt, bad
 
 
-def check_mask(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block=128):
-    n_diff, n_exempt, bad = mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block)
+def check_mask(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block=128, hist_only=False):
+    n_diff, n_exempt, bad = mask_exemptions(gpu_mask, ref_scores, ref_mask, q_start_pos, threshold, block,
+                                            hist_only)
     assert not bad, f"{len(bad)} unexplained mask differences (of {n_diff}), first {bad[:5]}"
     return n_diff, n_exempt
 
