@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="every (stride, threshold) of the workload, one line each")
     ap.add_argument("--estimator", choices=("full", "downsampled"), default="full",
                     help="downsampled: cache blocks chosen from K[::stride] of the history (cache-block workloads)")
+    ap.add_argument("--offload", action="store_true",
+                    help="history K/V in pinned host cache blocks, kept blocks copied back through a device ring")
+    ap.add_argument("--group", type=int, default=8, help="cache blocks per ring group (offload)")
     return ap.parse_args()
 
 
@@ -216,7 +219,7 @@ def main():
     w = dict(base)
     w["stride"] = a.stride if a.stride is not None else w.get("stride", 8)
     w["threshold"] = a.threshold if a.threshold is not None else w.get("threshold", 0.9)
-    out = measure(a, w, q, k, v)
+    out = measure_offload(a, w, q, k, v) if a.offload else measure(a, w, q, k, v)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups, w)
     print(json.dumps(out))
@@ -371,6 +374,54 @@ def measure(a, w, q, k, v):
     if a.estimator == "downsampled":
         out["vs_full_estimator"] = compare_estimators(run, q, k, v, w, starts)
     return out
+
+
+def measure_offload(a, w, q, k, v):
+    """The step with the history in pinned host memory (includes the host <-> device copies)."""
+    import torch
+    from block_sparse_attention_xattn_amd.offload import OffloadedChunkedPrefill
+    cb = w.get("cache_block", 1024)
+    starts = [w["q_start_pos"]] if "q_start_pos" in w else None
+    run = OffloadedChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
+                                  cache_block=cb, group=a.group, chunk_starts=starts)
+    run.prepare()
+    torch.cuda.synchronize()
+    for _ in range(a.warmup):
+        for p in run.starts:
+            run.run_chunk(p)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for p in run.starts:
+            run.run_chunk(p)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    d, hq, blk = w["d"], w["hq"], 128
+    nqb = w["chunk"] // blk
+    per_tile = 4.0 * d * blk * blk
+    block_bytes = cb * w["hkv"] * d * 2
+    flops = h2d = d2h = kept = avail = 0
+    for p in run.starts:
+        kp = run.kept.get(p, [])
+        kept += len(kp)
+        avail += p // cb
+        flops += per_tile * hq * nqb * (len(kp) * (cb // blk) + (nqb + 1) / 2)
+        h2d += 2 * block_bytes * len(kp)
+        d2h += 2 * block_bytes * (w["chunk"] // cb)
+    tokens = len(run.starts) * w["chunk"]
+    return {
+        "metric": "sparse prefill tokens/s per layer with the history offloaded to host memory (PCIe-inclusive)",
+        "value": round(tokens / (step_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": hq, "kv_heads": w["hkv"],
+                   "head_dim": d, "stride": w["stride"], "threshold": w["threshold"], "cache_block": cb,
+                   "ring_group": a.group, "estimator": "downsampled", "offload": True},
+        "kept_cache_blocks": kept, "history_cache_blocks": avail,
+        "host_to_device_gb_per_step": round(h2d / 1e9, 3), "device_to_host_gb_per_step": round(d2h / 1e9, 3),
+        "host_to_device_gbs": round(h2d / (step_ms * 1e-3) / 1e9, 1),
+        "attention_tflops": round(flops / (step_ms * 1e-3) / 1e12, 1),
+    }
 
 
 def compare_estimators(run, q, k, v, w, starts):

@@ -78,6 +78,12 @@ def _declare(lib):
     lib.xattn_estimate_history_ds.restype = ctypes.c_int
     lib.xattn_estimate_history_ds.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32, I32,
                                               I32, F, P, P, P, SZ, P]
+    lib.xattn_offload_blocks.restype = ctypes.c_int
+    lib.xattn_offload_blocks.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I32, I32, I32, I32, P, P, I64, I64,
+                                         P, P]
+    lib.bsa_history_offloaded.restype = ctypes.c_int
+    lib.bsa_history_offloaded.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I32, I32, I64, P, P, I64, I32, P, I32,
+                                          I32, P, P, P, P, P, P, P, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -336,6 +342,56 @@ def xattn_estimate_history_ds(q, k_ds, stride: int, threshold: float, block: int
                                            float(threshold), _ptr(block_scores), _ptr(block_mask), _ptr(ws),
                                            ws.numel(), _stream(stream)))
     return block_scores, block_mask
+
+
+class OffloadedKV:
+    """Host store of K / packed-V cache blocks (pinned) and the device ring (see xattn.h).
+
+    n_blocks cache blocks of cache_block tokens; the ring holds 2 * group blocks; staging holds the packed V of
+    up to max_offload_blocks blocks per xattn_offload_blocks call.
+    """
+
+    def __init__(self, n_blocks: int, num_kv_heads: int, head_dim: int, device, cache_block: int = 1024,
+                 group: int = 8, max_offload_blocks: int = 8):
+        self.n_blocks, self.hkv, self.d = n_blocks, num_kv_heads, head_dim
+        self.cache_block, self.group, self.max_offload = cache_block, group, max_offload_blocks
+        elems = cache_block * num_kv_heads * head_dim
+        self.host_k = torch.empty(n_blocks * elems, dtype=torch.bfloat16, pin_memory=True)
+        self.host_vt = torch.empty(n_blocks * elems, dtype=torch.bfloat16, pin_memory=True)
+        self.ring_k = torch.empty(2 * group * cache_block, num_kv_heads, head_dim, dtype=torch.bfloat16,
+                                  device=device)
+        self.ring_vt = workspace(2 * group * elems * 2, device)
+        self.staging = workspace(max_offload_blocks * elems * 2, device)
+        self.copy_stream = torch.cuda.Stream(device)
+
+
+def xattn_offload_blocks(store: OffloadedKV, k, v, first_block: int, stream=None):
+    """Store the cache blocks of k / v (device, len a multiple of cache_block) as host blocks first_block ..."""
+    _qkv_check(k, "k")
+    _qkv_check(v, "v")
+    n = k.shape[0] // store.cache_block
+    if n * store.cache_block != k.shape[0] or n > store.max_offload or first_block + n > store.n_blocks:
+        raise XattnError(XA_EINVAL, "offload: whole cache blocks, at most max_offload_blocks, within the store")
+    _check(lib().xattn_offload_blocks(_ptr(k), k.stride(0), k.stride(1), _ptr(v), v.stride(0), v.stride(1),
+                                      _dtype_code(k), n, store.hkv, store.d, store.cache_block,
+                                      ctypes.c_void_p(store.host_k.data_ptr()),
+                                      ctypes.c_void_p(store.host_vt.data_ptr()), store.n_blocks, first_block,
+                                      _ptr(store.staging), _stream(stream)))
+
+
+def bsa_history_offloaded(q, q_start_pos: int, store: OffloadedKV, keep, out, lse, part_out, part_lse,
+                          stream=None):
+    """Attention of q over the host cache blocks `keep` (ids, no causal rule) through the ring (see xattn.h)."""
+    _qkv_check(q, "q")
+    q_len, hq, d = q.shape
+    ids = (ctypes.c_int32 * max(len(keep), 1))(*[int(i) for i in keep])
+    _check(lib().bsa_history_offloaded(_ptr(q), q.stride(0), q.stride(1), _dtype_code(q), q_len, hq, store.hkv, d,
+                                       q_start_pos, ctypes.c_void_p(store.host_k.data_ptr()),
+                                       ctypes.c_void_p(store.host_vt.data_ptr()), store.n_blocks,
+                                       store.cache_block, ids, len(keep), store.group, _ptr(store.ring_k),
+                                       _ptr(store.ring_vt), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
+                                       _stream(stream), store.copy_stream.cuda_stream))
+    return out, lse
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
-SOURCES = ["abi.hip", "merge.hip", "reduce.hip", "bsa.hip", "estimate.hip"]
+SOURCES = ["abi.hip", "merge.hip", "reduce.hip", "bsa.hip", "estimate.hip", "offload.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

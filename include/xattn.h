@@ -286,6 +286,53 @@ xa_status_t xattn_estimate_history_ds(const void* q, int64_t q_tok_stride, int64
                                       void* workspace, size_t workspace_bytes, xa_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Offloaded history (cache blocks in pinned host memory)
+ *
+ * XAttentionBSAPolicy page, compute_chunked_prefill with the offload engine
+ * (the history comes from CPU cache blocks through a ring of GPU slots) and
+ * task plan page, "核心设计理解" (1 CPU block = 8 BSA blocks).  A host store
+ * of n_host_blocks cache blocks of cache_block tokens holds K token-major,
+ * host_k [n_host_blocks * cache_block][num_kv_heads][head_dim], and V packed
+ * for the attention kernel over the whole store, host_vt [num_kv_heads]
+ * [head_dim][n_host_blocks * cache_block] (keys permuted in groups of 16 as
+ * bsa_pack_v does); bf16, pinned memory for asynchronous copies, owned by the
+ * caller.  Consecutive cache blocks are thus one K copy and one 2-D V copy.
+ *
+ * xattn_offload_blocks: stores n_blocks consecutive cache blocks of k / v
+ *   (device, [n_blocks * cache_block][num_kv_heads][head_dim], head_dim
+ *   contiguous and heads contiguous within a token for k) as host blocks
+ *   first_block ..; V is packed into staging_vt (device, 256-byte aligned,
+ *   n_blocks * num_kv_heads * head_dim * cache_block bf16) first.  Copies are
+ *   queued on stream; host memory is written when the stream reaches them.
+ * bsa_history_offloaded: attention of the query chunk q ([q_len][num_q_heads]
+ *   [head_dim] bf16, strided; global position q_start_pos) over every token of
+ *   the host cache blocks keep[0 .. n_keep-1] (HOST array, ids < n_host_blocks)
+ *   without the causal rule (history).  The blocks move in groups of `group`
+ *   into a device ring of 2 * group blocks -- ring_k [2*group*cache_block]
+ *   [num_kv_heads][head_dim] and ring_vt, packed V of capacity 2 * group *
+ *   cache_block (256-byte aligned) -- on copy_stream (one K copy and one
+ *   2-D V copy per run of consecutive ids), the attention over a
+ *   group runs on stream once its copies land (events order the two streams
+ *   both ways), and each group's result (part_out / part_lse, same shapes as
+ *   out / lse) is merged into out / lse by LSE (attn_merge).  out bf16
+ *   [q_len][num_q_heads][head_dim], lse float [num_q_heads][q_len]; n_keep = 0
+ *   gives out 0 and lse -inf.  Copies into the ring wait for all work queued on
+ *   stream before the call.  Errors as for bsa_prefill_packed.
+ * ------------------------------------------------------------------------ */
+xa_status_t xattn_offload_blocks(const void* k, int64_t k_tok_stride, int64_t k_head_stride, const void* v,
+                                 int64_t v_tok_stride, int64_t v_head_stride, xa_dtype_t dtype, int32_t n_blocks,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t cache_block, void* host_k,
+                                 void* host_vt, int64_t n_host_blocks, int64_t first_block, void* staging_vt,
+                                 xa_stream_t stream);
+
+xa_status_t bsa_history_offloaded(const void* q, int64_t q_tok_stride, int64_t q_head_stride, xa_dtype_t dtype,
+                                  int64_t q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int64_t q_start_pos, const void* host_k, const void* host_vt,
+                                  int64_t n_host_blocks, int32_t cache_block, const int32_t* keep, int32_t n_keep,
+                                  int32_t group, void* ring_k, void* ring_vt, void* out, float* lse,
+                                  void* part_out, float* part_lse, xa_stream_t stream, xa_stream_t copy_stream);
+
+/* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)
  *
  * nano-vllm CLAUDE.md, "Online Softmax Merge - Triton Fused Kernel":
