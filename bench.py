@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain device copy of this many MiB")
     ap.add_argument("--sweep", action="store_true", help="every (stride, threshold) of the workload, one line each")
     ap.add_argument("--estimator", choices=("full", "downsampled"), default="full",
-                    help="downsampled: cache blocks chosen from K[::stride] of the history (cache-block workloads)")
+                    help="downsampled: cache blocks chosen from K[::stride] of the history (cache-block workloads); "
+                         "with --offload, full streams the host-resident history K through the ring")
     ap.add_argument("--offload", action="store_true",
                     help="history K/V in pinned host cache blocks, kept blocks copied back through a device ring")
     ap.add_argument("--group", type=int, default=8, help="cache blocks per ring group (offload)")
@@ -382,8 +383,10 @@ def measure_offload(a, w, q, k, v):
     from block_sparse_attention_xattn_amd.offload import OffloadedChunkedPrefill
     cb = w.get("cache_block", 1024)
     starts = [w["q_start_pos"]] if "q_start_pos" in w else None
+    # with the history on the host the full estimate streams it through the ring
+    est = "downsampled" if a.estimator == "downsampled" else "streamed"
     run = OffloadedChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
-                                  cache_block=cb, group=a.group, chunk_starts=starts)
+                                  cache_block=cb, group=a.group, chunk_starts=starts, estimator=est)
     run.prepare()
     torch.cuda.synchronize()
     for _ in range(a.warmup):
@@ -406,7 +409,7 @@ def measure_offload(a, w, q, k, v):
         kept += len(kp)
         avail += p // cb
         flops += per_tile * hq * nqb * (len(kp) * (cb // blk) + (nqb + 1) / 2)
-        h2d += 2 * block_bytes * len(kp)
+        h2d += 2 * block_bytes * len(kp) + (block_bytes * (p // cb) if est == "streamed" else 0)
         d2h += 2 * block_bytes * (w["chunk"] // cb)
     tokens = len(run.starts) * w["chunk"]
     return {
@@ -416,7 +419,7 @@ def measure_offload(a, w, q, k, v):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": hq, "kv_heads": w["hkv"],
                    "head_dim": d, "stride": w["stride"], "threshold": w["threshold"], "cache_block": cb,
-                   "ring_group": a.group, "estimator": "downsampled", "offload": True},
+                   "ring_group": a.group, "estimator": est, "offload": True},
         "kept_cache_blocks": kept, "history_cache_blocks": avail,
         "host_to_device_gb_per_step": round(h2d / 1e9, 3), "device_to_host_gb_per_step": round(d2h / 1e9, 3),
         "host_to_device_gbs": round(h2d / (step_ms * 1e-3) / 1e9, 1),

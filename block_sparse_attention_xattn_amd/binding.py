@@ -84,6 +84,8 @@ def _declare(lib):
     lib.bsa_history_offloaded.restype = ctypes.c_int
     lib.bsa_history_offloaded.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I32, I32, I64, P, P, I64, I32, P, I32,
                                           I32, P, P, P, P, P, P, P, P]
+    lib.xattn_estimate_offloaded.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I32, I32, I64, P,
+                                             I64, I32, I32, P, I32, I32, F, P, P, P, SZ, P, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -392,6 +394,32 @@ def bsa_history_offloaded(q, q_start_pos: int, store: OffloadedKV, keep, out, ls
                                        _ptr(store.ring_vt), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
                                        _stream(stream), store.copy_stream.cuda_stream))
     return out, lse
+
+
+def xattn_estimate_offloaded(q, k_cur, q_start_pos: int, store: OffloadedKV, stride: int = 8,
+                             threshold: float = 0.9, block: int = 128, block_scores=None, block_mask=None, ws=None,
+                             stream=None):
+    """xattn_estimate of q against host cache blocks 0 .. q_start_pos/cache_block - 1 of store and the chunk's
+    own keys k_cur, the history streamed through the store's ring (see xattn.h).  Returns (scores, mask)."""
+    _qkv_check(q, "q")
+    _qkv_check(k_cur, "k_cur")
+    q_len, hq, d = q.shape
+    k_len = q_start_pos + q_len
+    n_qb, nkb = q_len // block, k_len // block
+    if block_scores is None:
+        block_scores = torch.empty(hq, n_qb, nkb, dtype=torch.float32, device=q.device)
+    if block_mask is None:
+        block_mask = torch.empty(hq, n_qb, nkb, dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = workspace(xattn_estimate_workspace_size(q_len, k_len, hq, store.hkv, d, stride, block, XA_BF16),
+                       q.device)
+    _check(lib().xattn_estimate_offloaded(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cur), k_cur.stride(0),
+                                          k_cur.stride(1), _dtype_code(q), q_len, hq, store.hkv, d, q_start_pos,
+                                          ctypes.c_void_p(store.host_k.data_ptr()), store.n_blocks,
+                                          store.cache_block, store.group, _ptr(store.ring_k), stride, block,
+                                          float(threshold), _ptr(block_scores), _ptr(block_mask), _ptr(ws),
+                                          ws.numel(), _stream(stream), store.copy_stream.cuda_stream))
+    return block_scores, block_mask
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -131,6 +131,7 @@ xa_status_t estimate_core(const char* fn, const void* q, int64_t q_tok, int64_t 
   p.R = (int)R;
   p.N = (int)N;
   p.nkb = (int)nkb;
+  p.nkb_ld = (int)nkb;
   p.n_rt = (int)((R + 127) / 128);
   p.n_ct = (int)((N + 127) / 128);
   p.scale_log2 = kLog2e / ((float)stride * sqrtf((float)d));

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kEThreads) void est_gemm_kernel(EstParams P) {
   const int kvh = w / P.n_ct;
   const int h = kvh * P.group + j;
 
-  const int64_t cdiag = P.q_start / P.S;  // column c visible to row r iff c <= cdiag + r
+  const int64_t cdiag = P.q_start / P.S - P.c0;  // local column c visible to row r iff c <= cdiag + r
   const int r_hi = min(P.R - 1, rt * 128 + 127);
   if ((int64_t)ct * 128 > cdiag + r_hi) return;  // tile entirely right of the causal limit
 
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kEThreads) void est_gemm_kernel(EstParams P) {
       s += __shfl_xor(s, 32);
       const int kb = w_c0 / (2 * HALF) + g0 / HALF;
       if (hh == 0 && r < P.R && kb < P.nkb)
-        P.lse_part[((int64_t)h * P.nkb + kb) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
+        P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kb) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
     }
   }
 }
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
   const int kvh = w / n_ct;
   const int h = kvh * P.group + j;
 
-  const int64_t cdiag = P.q_start / P.S;
+  const int64_t cdiag = P.q_start / P.S - P.c0;
   const int r_hi = min(P.R - 1, rt * TILE + TILE - 1);
   if ((int64_t)ct * TILE > cdiag + r_hi) return;
 
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
       s += __shfl_xor(s, 32);
       const int kbk = w_c0 / (2 * HALF) + g0 / HALF;
       if (hh == 0 && r < P.R && kbk < P.nkb)
-        P.lse_part[((int64_t)h * P.nkb + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
+        P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
     }
   }
 }

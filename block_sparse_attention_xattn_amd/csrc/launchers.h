@@ -38,7 +38,10 @@ struct EstParams {
   int64_t q_len, k_len, q_start;
   int hq, hkv, group, S, b, R, N, nkb, n_rt, n_ct;
   float scale_log2;
-  float* lse_part;  // [hq][nkb][R], log2 units
+  // K row 0 is reshaped column c0 (global) = key block kb0; lse_part rows hold nkb_ld key blocks
+  int64_t c0;
+  int kb0, nkb_ld;
+  float* lse_part;  // [hq][nkb_ld][R], log2 units; this call writes key blocks kb0 .. kb0 + nkb - 1
 };
 
 // Block sums + threshold selection (estimate.hip).

@@ -159,3 +159,154 @@ extern "C" xa_status_t bsa_history_offloaded(const void* q, int64_t q_tok, int64
   }
   return XA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Estimate against host-resident history keys
+//
+// XAttentionBSAPolicy page, select_blocks (the estimate over K that arrives
+// from the CPU cache one chunk of blocks at a time: partial row statistics
+// per key chunk, their merge, then block sums).  The estimate GEMM already
+// leaves one log-sum-exp per (reshaped row, key block); each group of cache
+// blocks copied into the ring fills its key blocks' entries, the chunk's own
+// keys fill theirs, and one selection pass merges the row statistics and
+// forms the block sums, so every history key crosses PCIe once.
+// ---------------------------------------------------------------------------
+namespace {
+using xa::EstParams;
+using xa::SelParams;
+
+EstParams est_params(const bf16* q, int64_t q_tok, int64_t q_head, int64_t q_len, int64_t q_start, int32_t hq,
+                     int32_t hkv, int32_t d, int32_t stride, float* lse, int64_t nkb_total) {
+  EstParams p{};
+  p.q_hi = q;
+  p.q_tok = q_tok;
+  p.q_head = q_head;
+  p.q_len = q_len;
+  p.q_start = q_start;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.S = stride;
+  p.b = 128 / stride;
+  p.R = (int)(q_len / stride);
+  p.n_rt = (p.R + 127) / 128;
+  p.scale_log2 = xa::kLog2e / ((float)stride * sqrtf((float)d));
+  p.nkb_ld = (int)nkb_total;
+  p.lse_part = lse;
+  return p;
+}
+
+// keys [key0, key0 + n_keys) of the layer, rows of k with the given strides
+hipError_t est_keys(EstParams p, const bf16* k, int64_t k_tok, int64_t k_head, int64_t key0, int64_t n_keys, int d,
+                    hipStream_t s) {
+  p.k_hi = k;
+  p.k_tok = k_tok;
+  p.k_head = k_head;
+  p.k_len = n_keys;
+  p.N = (int)(n_keys / p.S);
+  p.n_ct = (p.N + 127) / 128;
+  p.c0 = key0 / p.S;
+  p.kb0 = (int)(key0 / 128);
+  p.nkb = (int)(n_keys / 128);
+  return d == 128 ? xa::launch_est_gemm<128, false>(p, s) : xa::launch_est_gemm<64, false>(p, s);
+}
+}  // namespace
+
+extern "C" xa_status_t xattn_estimate_offloaded(const void* q, int64_t q_tok, int64_t q_head, const void* k_cur,
+                                                int64_t kc_tok, int64_t kc_head, xa_dtype_t dtype, int64_t q_len,
+                                                int32_t hq, int32_t hkv, int32_t d, int64_t q_start_pos,
+                                                const void* host_k, int64_t n_host_blocks, int32_t cache_block,
+                                                int32_t group, void* ring_k, int32_t stride, int32_t block,
+                                                float threshold, float* block_scores, uint8_t* block_mask,
+                                                void* workspace, size_t ws_bytes, xa_stream_t stream,
+                                                xa_stream_t copy_stream) {
+  const char* fn = "xattn_estimate_offloaded";
+  if (dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: XA_BF16 only", fn);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(XA_EINVAL, "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn, hq, hkv);
+  if (d != 64 && d != 128) return fail(XA_EUNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, d);
+  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (stride != 2 && stride != 4 && stride != 8 && stride != 16)
+    return fail(XA_EUNSUPPORTED, "%s: stride %d not in {2, 4, 8, 16}", fn, stride);
+  if (cache_block <= 0 || cache_block % 128 != 0)
+    return fail(XA_EINVAL, "%s: cache_block must be a positive multiple of 128 (got %d)", fn, cache_block);
+  if (group <= 0 || (int64_t)group * cache_block * 2 > ((int64_t)1 << 30))
+    return fail(XA_EINVAL, "%s: group must be positive and the ring at most 2^30 tokens", fn);
+  if (q_len <= 0 || q_len % 128 != 0)
+    return fail(XA_EINVAL, "%s: q_len %lld must be a positive multiple of 128", fn, (long long)q_len);
+  if (q_start_pos < 0 || q_start_pos % cache_block != 0 || q_start_pos / cache_block > n_host_blocks)
+    return fail(XA_EINVAL, "%s: q_start_pos %lld must be whole cache blocks held by the %lld host blocks", fn,
+                (long long)q_start_pos, (long long)n_host_blocks);
+  const int64_t k_len = q_start_pos + q_len;
+  const int64_t nkb = k_len / 128;
+  if (nkb > 8192) return fail(XA_EUNSUPPORTED, "%s: k_len / block = %lld exceeds 8192 key blocks", fn, (long long)nkb);
+  if (!(threshold >= 0.f)) return fail(XA_EINVAL, "%s: threshold must be >= 0", fn);  // NaN fails too
+  if (!q || !k_cur || !ring_k || !block_scores || !block_mask || (q_start_pos > 0 && !host_k))
+    return fail(XA_EINVAL, "%s: null pointer", fn);
+  if (q_tok % 8 || q_head % 8 || (uintptr_t)q % 16 || kc_tok % 8 || kc_head % 8 || (uintptr_t)k_cur % 16 ||
+      (uintptr_t)ring_k % 16)
+    return fail(XA_EINVAL, "%s: q, k_cur and ring_k must be 16-byte aligned with strides multiples of 8", fn);
+  const size_t need = xattn_estimate_workspace_size(q_len, k_len, hq, hkv, d, stride, block, XA_BF16);
+  if (!workspace || ws_bytes < need || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need, ws_bytes);
+  if ((int64_t)hq * nkb * q_len > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
+  float* lse = static_cast<float*>(workspace);
+  const EstParams p0 = est_params(static_cast<const bf16*>(q), q_tok, q_head, q_len, q_start_pos, hq, hkv, d, stride,
+                                  lse, nkb);
+  hipError_t e;
+  // the chunk's own keys first: they need no copy
+  if ((e = est_keys(p0, static_cast<const bf16*>(k_cur), kc_tok, kc_head, q_start_pos, q_len, d, s)) != hipSuccess)
+    return fail(XA_EHIP, "%s: estimate GEMM launch failed: %s", fn, hipGetErrorString(e));
+  const int64_t cb = cache_block;
+  const int64_t row = (int64_t)hkv * d;
+  const size_t block_bytes = (size_t)cb * row * 2;
+  const int64_t n_hist = q_start_pos / cb;
+  if (n_hist > 0) {
+    Events ev;  // [0] start, [1..2] half copied, [3..4] half consumed
+    if ((e = ev.create()) != hipSuccess)
+      return fail(XA_EHIP, "%s: event creation failed: %s", fn, hipGetErrorString(e));
+    if ((e = hipEventRecord(ev.e[0], s)) != hipSuccess || (e = hipStreamWaitEvent(cs, ev.e[0], 0)) != hipSuccess)
+      return fail(XA_EHIP, "%s: stream ordering failed: %s", fn, hipGetErrorString(e));
+    const int64_t n_groups = (n_hist + group - 1) / group;
+    for (int64_t g = 0; g < n_groups; ++g) {
+      const int half = (int)(g & 1);
+      const int64_t base = (int64_t)half * group;
+      const int64_t n_g = n_hist - g * group < group ? n_hist - g * group : group;
+      if (g >= 2 && (e = hipStreamWaitEvent(cs, ev.e[3 + half], 0)) != hipSuccess)
+        return fail(XA_EHIP, "%s: stream ordering failed: %s", fn, hipGetErrorString(e));
+      // blocks g*group .. are consecutive on the host and in the ring half: one copy
+      e = hipMemcpyAsync(static_cast<char*>(ring_k) + (size_t)base * block_bytes,
+                         static_cast<const char*>(host_k) + (size_t)(g * group) * block_bytes,
+                         (size_t)n_g * block_bytes, hipMemcpyHostToDevice, cs);
+      if (e != hipSuccess) return fail(XA_EHIP, "%s: copy to the ring failed: %s", fn, hipGetErrorString(e));
+      if ((e = hipEventRecord(ev.e[1 + half], cs)) != hipSuccess ||
+          (e = hipStreamWaitEvent(s, ev.e[1 + half], 0)) != hipSuccess)
+        return fail(XA_EHIP, "%s: stream ordering failed: %s", fn, hipGetErrorString(e));
+      if ((e = est_keys(p0, static_cast<const bf16*>(ring_k) + (size_t)base * cb * row, row, d, g * group * cb,
+                        n_g * cb, d, s)) != hipSuccess)
+        return fail(XA_EHIP, "%s: estimate GEMM launch failed: %s", fn, hipGetErrorString(e));
+      if ((e = hipEventRecord(ev.e[3 + half], s)) != hipSuccess)
+        return fail(XA_EHIP, "%s: event record failed: %s", fn, hipGetErrorString(e));
+    }
+  }
+  SelParams sp{};
+  sp.lse_part = lse;
+  sp.R = p0.R;
+  sp.nkb = (int)nkb;
+  sp.npow_cap = 1;
+  while (sp.npow_cap < sp.nkb) sp.npow_cap <<= 1;
+  sp.b = p0.b;
+  sp.hq = hq;
+  sp.n_qb = (int)(q_len / 128);
+  sp.hist_only = 0;
+  sp.cur = q_start_pos / 128;
+  sp.threshold = threshold;
+  sp.scores = block_scores;
+  sp.mask = block_mask;
+  if ((e = xa::launch_est_select(sp, s)) != hipSuccess)
+    return fail(XA_EHIP, "%s: selection launch failed: %s", fn, hipGetErrorString(e));
+  return XA_OK;
+}

@@ -10,9 +10,15 @@ the blocks already copied), the chunk's own keys are attended densely with the
 causal rule, the two parts are merged by LSE, and the chunk's K / V are then
 offloaded as cache blocks for the chunks after it.
 
-Device memory per layer: the chunk's rows, K[::stride] of the whole layer, a
-ring of 2 x group cache blocks of K and packed V, and per-chunk buffers; the
-history K / V live in pinned host memory.
+With estimator="streamed" the chunk's estimate is instead the full one of
+select_blocks on the XAttentionBSAPolicy page, computed as the history K
+arrives from the host through the same ring (xattn_estimate_offloaded); its
+mask is reduced to cache blocks with the first and last history cache block
+forced, as the resident path does, and no K[::stride] is kept.
+
+Device memory per layer: the chunk's rows, K[::stride] of the whole layer
+(downsampled estimator), a ring of 2 x group cache blocks of K and packed V,
+and per-chunk buffers; the history K / V live in pinned host memory.
 """
 from __future__ import annotations
 
@@ -25,7 +31,10 @@ class OffloadedChunkedPrefill:
     """q, k, v [L, H, d] bf16 on the GPU (only the current chunk's rows are read there); `starts` chunks run."""
 
     def __init__(self, q, k, v, chunk: int, stride: int, threshold: float, cache_block: int = 1024,
-                 group: int = 8, chunk_starts=None, block: int = 128):
+                 group: int = 8, chunk_starts=None, block: int = 128, estimator: str = "downsampled"):
+        if estimator not in ("downsampled", "streamed"):
+            raise ValueError("estimator must be 'downsampled' or 'streamed'")
+        self.estimator = estimator
         self.q, self.k, self.v = q, k, v
         self.L, self.hq, self.d = q.shape
         self.hkv = k.shape[1]
@@ -37,17 +46,23 @@ class OffloadedChunkedPrefill:
         self.starts = list(range(0, self.L, chunk)) if chunk_starts is None else list(chunk_starts)
         self.store = B.OffloadedKV(self.L // cache_block, self.hkv, self.d, dev, cache_block, group,
                                    max_offload_blocks=max(chunk // cache_block, 1))
-        self.k_ds = torch.empty(self.L // stride, self.hkv, self.d, dtype=k.dtype, device=dev)
         self.packed = B.PackedV(chunk, self.hkv, self.d, q.dtype, dev)
-        bds = block // stride
         max_p = max(self.starts)
-        self.est_ws = B.workspace(max([B.xattn_estimate_history_ds_workspace_size(
-            chunk, p // stride, self.hq, self.hkv, self.d, stride, block) for p in self.starts if p > 0] or [0]), dev)
-        n_hist_blocks = max(max_p // block, 1)
-        self.scores = torch.empty(self.hq, chunk // bds, n_hist_blocks, dtype=torch.float32, device=dev)
-        self.mask = torch.empty(self.hq, chunk // bds, n_hist_blocks, dtype=torch.uint8, device=dev)
+        if estimator == "downsampled":
+            self.k_ds = torch.empty(self.L // stride, self.hkv, self.d, dtype=k.dtype, device=dev)
+            est_ws = max([B.xattn_estimate_history_ds_workspace_size(chunk, p // stride, self.hq, self.hkv, self.d,
+                                                                      stride, block) for p in self.starts if p > 0]
+                         or [0])
+            rows, cols = chunk // (block // stride), max(max_p // block, 1)
+        else:
+            est_ws = max(B.xattn_estimate_workspace_size(chunk, p + chunk, self.hq, self.hkv, self.d, stride, block)
+                         for p in self.starts)
+            rows, cols = chunk // block, (max_p + chunk) // block
+        self.est_ws = B.workspace(est_ws, dev)
+        self.scores = torch.empty(self.hq, rows, cols, dtype=torch.float32, device=dev)
+        self.mask = torch.empty(self.hq, rows, cols, dtype=torch.uint8, device=dev)
         ncb = max(max_p // cache_block, 1)
-        self.keep_per_head = torch.empty(self.hq, chunk // bds, ncb, dtype=torch.uint8, device=dev)
+        self.keep_per_head = torch.empty(self.hq, rows, ncb, dtype=torch.uint8, device=dev)
         self.keep_any = torch.empty(ncb, dtype=torch.uint8, device=dev)
         self.keep_any_blocks = torch.empty(ncb * (cache_block // block), dtype=torch.uint8, device=dev)
         self.keep_host = torch.empty(ncb, dtype=torch.uint8, pin_memory=True)
@@ -65,18 +80,25 @@ class OffloadedChunkedPrefill:
         for b0 in range(0, p0, self.chunk):
             n = min(self.chunk, p0 - b0)
             B.xattn_offload_blocks(self.store, self.k[b0:b0 + n], self.v[b0:b0 + n], b0 // self.cb)
-        if p0 > 0:
+        if p0 > 0 and self.estimator == "downsampled":
             B.xattn_downsample_keys(self.k[:p0], self.stride, self.k_ds, 0)
 
     def select(self, p: int):
         """Queue the chunk's estimate and cache-block union; the kept ids reach the host with the returned event."""
         c = self.chunk
-        n_blk = p // self.block
         ncb = p // self.cb
-        sc, m = self.scores[:, :, :n_blk], self.mask[:, :, :n_blk]
-        B.xattn_estimate_history_ds(self.q[p:p + c], self.k_ds[:p // self.stride], self.stride, self.threshold,
-                                    self.block, block_scores=sc, block_mask=m, ws=self.est_ws)
-        B.xattn_mask_to_cache_blocks(m, 0, ncb, self.cb // self.block, False,
+        if self.estimator == "downsampled":
+            n_blk = p // self.block
+            sc, m = self.scores[:, :, :n_blk], self.mask[:, :, :n_blk]
+            B.xattn_estimate_history_ds(self.q[p:p + c], self.k_ds[:p // self.stride], self.stride, self.threshold,
+                                        self.block, block_scores=sc, block_mask=m, ws=self.est_ws)
+        else:
+            n_blk = (p + c) // self.block
+            sc, m = self.scores[:, :, :n_blk], self.mask[:, :, :n_blk]
+            B.xattn_estimate_offloaded(self.q[p:p + c], self.k[p:p + c], p, self.store, self.stride, self.threshold,
+                                       self.block, block_scores=sc, block_mask=m, ws=self.est_ws)
+        # the downsampled estimate keeps the union only; the full estimate also forces the first / last block
+        B.xattn_mask_to_cache_blocks(m, 0, ncb, self.cb // self.block, self.estimator == "streamed",
                                      keep_per_head=self.keep_per_head[:, :, :ncb], keep_any=self.keep_any[:ncb],
                                      keep_any_blocks=self.keep_any_blocks[:ncb * (self.cb // self.block)])
         self.keep_host[:ncb].copy_(self.keep_any[:ncb], non_blocking=True)
@@ -87,7 +109,8 @@ class OffloadedChunkedPrefill:
     def run_chunk(self, p: int):
         c = self.chunk
         qc = self.q[p:p + c]
-        B.xattn_downsample_keys(self.k[p:p + c], self.stride, self.k_ds, p // self.stride)
+        if self.estimator == "downsampled":
+            B.xattn_downsample_keys(self.k[p:p + c], self.stride, self.k_ds, p // self.stride)
         B.bsa_pack_v(self.v[p:p + c], self.packed, 0)
         lse = self.lse[p]
         if p > 0:

@@ -332,6 +332,37 @@ xa_status_t bsa_history_offloaded(const void* q, int64_t q_tok_stride, int64_t q
                                   int32_t group, void* ring_k, void* ring_vt, void* out, float* lse,
                                   void* part_out, float* part_lse, xa_stream_t stream, xa_stream_t copy_stream);
 
+/* xattn_estimate_offloaded: xattn_estimate (same scores and mask, bit for bit)
+ *   of the query chunk q ([q_len][num_q_heads][head_dim] bf16, global position
+ *   q_start_pos) against keys 0 .. q_start_pos + q_len - 1 where the history
+ *   keys 0 .. q_start_pos - 1 are the host cache blocks 0 .. q_start_pos /
+ *   cache_block - 1 of host_k (q_start_pos a multiple of cache_block) and the
+ *   chunk's own keys are k_cur ([q_len][num_kv_heads][head_dim] bf16 on the
+ *   device).  XAttentionBSAPolicy page, select_blocks: the estimate runs over
+ *   the keys as they arrive from the CPU cache, a group of cache blocks at a
+ *   time (per-row partial statistics per key chunk, merged before the block
+ *   sums).  Every history block passes once through ring_k (the K half of the
+ *   ring of bsa_history_offloaded, 2 * group * cache_block tokens): copies on
+ *   copy_stream, estimate GEMMs on stream, events both ways; the partial
+ *   log-sum-exp of each (row, key block) goes to the workspace and one
+ *   selection pass finishes on stream.  Workspace: xattn_estimate_workspace_
+ *   size(q_len, q_start_pos + q_len, ..., XA_BF16) bytes, 256-byte aligned.
+ *   block_scores / block_mask as for xattn_estimate ([num_q_heads][q_len /
+ *   128][(q_start_pos + q_len) / 128]).  Copies into the ring wait for all
+ *   work queued on stream before the call.  Errors: XA_EUNSUPPORTED for
+ *   other dtypes, head dims, strides or blocks; XA_EINVAL for shapes, null
+ *   pointers or alignment; XA_EWORKSPACE for a short workspace; nothing is
+ *   queued on an error.
+ */
+xa_status_t xattn_estimate_offloaded(const void* q, int64_t q_tok_stride, int64_t q_head_stride, const void* k_cur,
+                                     int64_t kc_tok_stride, int64_t kc_head_stride, xa_dtype_t dtype, int64_t q_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int64_t q_start_pos, const void* host_k, int64_t n_host_blocks,
+                                     int32_t cache_block, int32_t group, void* ring_k, int32_t stride,
+                                     int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
+                                     void* workspace, size_t workspace_bytes, xa_stream_t stream,
+                                     xa_stream_t copy_stream);
+
 /* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)
  *

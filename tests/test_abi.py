@@ -173,3 +173,42 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_offload_entry_points_reject(lib):
+    I32 = ctypes.c_int32
+    keep = (I32 * 2)(0, 9)
+
+    def off(n=4, first=0, n_host=8, d=128, cb=1024, stg=FAKE2, dt=B.XA_BF16):
+        return lib.xattn_offload_blocks(FAKE, 1024, 128, FAKE, 1024, 128, dt, n, 8, d, cb, FAKE, FAKE, n_host, first,
+                                        stg, None)
+    assert off(first=6) == B.XA_EINVAL                       # past the host store
+    assert off(n=-1) == B.XA_EINVAL
+    assert off(d=96) == B.XA_EUNSUPPORTED
+    assert off(cb=1000) == B.XA_EINVAL
+    assert off(stg=ctypes.c_void_p(0x200010)) == B.XA_EINVAL
+    assert off(dt=B.XA_F32) == B.XA_EUNSUPPORTED
+
+    def hist(ids=keep, n=2, group=2, rvt=FAKE2, dt=B.XA_BF16):
+        return lib.bsa_history_offloaded(FAKE, 4096, 128, dt, 1024, 32, 8, 128, 8192, FAKE, FAKE, 8, 1024, ids, n,
+                                         group, FAKE, rvt, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert hist() == B.XA_EINVAL                             # id 9 outside 8 host blocks
+    assert hist(ids=None, n=1) == B.XA_EINVAL
+    assert hist(n=1, group=0) == B.XA_EINVAL
+    assert hist(n=1, rvt=ctypes.c_void_p(0x200010)) == B.XA_EINVAL
+    assert hist(n=1, dt=B.XA_F32) == B.XA_EUNSUPPORTED
+
+    need = B.xattn_estimate_workspace_size(1024, 5120, 32, 8, 128, 8, 128, B.XA_BF16)
+
+    def est(p=4096, n_host=8, S=8, group=2, ring=FAKE2, ws=FAKE, wsb=need, tau=0.9, dt=B.XA_BF16):
+        return lib.xattn_estimate_offloaded(FAKE, 4096, 128, FAKE, 1024, 128, dt, 1024, 32, 8, 128, p, FAKE, n_host,
+                                            1024, group, ring, S, 128, tau, FAKE, FAKE, ws, wsb, None, None)
+    assert est(p=1000) == B.XA_EINVAL                        # not whole cache blocks
+    assert est(p=12288) == B.XA_EINVAL                       # more history than the host store holds
+    assert est(S=3) == B.XA_EUNSUPPORTED
+    assert est(group=0) == B.XA_EINVAL
+    assert est(ring=ctypes.c_void_p(0x200008)) == B.XA_EINVAL
+    assert est(wsb=need - 1) == B.XA_EWORKSPACE
+    assert est(ws=ctypes.c_void_p(0x100010)) == B.XA_EWORKSPACE
+    assert est(tau=float("nan")) == B.XA_EINVAL
+    assert est(dt=B.XA_F32) == B.XA_EUNSUPPORTED

@@ -12,6 +12,13 @@
 The host packed V is bsa_pack_v of the whole store, byte for byte; keep
 lists include runs of consecutive ids (one copy per run) and runs cut by a
 group boundary.
+
+The estimate over host-resident history keys (xattn_estimate_offloaded)
+equals xattn_estimate over the same keys on the device bit for bit, and the
+oracle's three-stage streaming form (key chunks of one ring group) to the
+score / mask tolerances; the offloaded prefill with that estimate keeps the
+cache blocks that the oracle's estimate and reducer keep and matches the
+oracle's attention over them.
 """
 import numpy as np
 import pytest
@@ -106,6 +113,58 @@ def test_offloaded_chunked_prefill_16k():
     assert off.kept[p] == keep_res
     _, rm = O.estimate_history_downsampled(_np(q[p:]), O.downsample_keys(_np(k[:p]), S), S, tau)
     ref_keep = O.history_cache_blocks_downsampled(rm, p // 1024)
+    keep = O.expand_cache_keep(ref_keep, 8, p // 128)
+    g = w["hq"] // w["hkv"]
+    for h, qb in [(0, 0), (13, 17), (31, 31)]:
+        rows = slice(p + qb * 128, p + (qb + 1) * 128)
+        kvh = h // g
+        o1, l1 = O.bsa(_np(q[rows, h:h + 1]), _np(k[:p, kvh:kvh + 1]), _np(v[:p, kvh:kvh + 1]), p + qb * 128, 0,
+                       keep[None, None, :], 0, False)
+        o2, l2 = O.bsa(_np(q[rows, h:h + 1]), _np(k[p:, kvh:kvh + 1]), _np(v[p:, kvh:kvh + 1]), p + qb * 128, p,
+                       None, 0, True)
+        ro, rl = O.merge(o1, l1, o2, l2)
+        PAR.check_out_lse(_np(off.out[rows, h:h + 1]), _np(off.lse[p][h:h + 1, qb * 128:(qb + 1) * 128]), ro, rl,
+                          PAR.OUT_ATOL_BF16)
+
+
+@pytest.mark.parametrize("group,q_start", [(2, 12288), (8, 12288), (2, 4096), (8, 0)])
+def test_estimate_offloaded(offloaded, group, q_start):
+    from block_sparse_attention_xattn_amd import binding as B
+    q, k, cb = offloaded["q"], offloaded["k"], offloaded["cb"]
+    S, tau = 8, 0.9
+    st = offloaded["stores"][group]
+    k_cur = _rand((1024, k.shape[1], k.shape[2]), 23)
+    qd, kcd = q.to(DEV), k_cur.to(DEV)
+    sc, m = B.xattn_estimate_offloaded(qd, kcd, q_start, st, S, tau)
+    k_all = torch.cat([k[:q_start], k_cur])
+    rs, rm = B.xattn_estimate(qd, k_all.to(DEV), q_start, S, tau)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, rs) and torch.equal(m, rm)
+    ref_s = O.estimate_scores_kv_chunked(_np(q), _np(k_all), q_start, S, 128, group * cb)
+    ref_m = O.select_blocks(ref_s, q_start, tau)
+    PAR.check_scores(_np(sc), ref_s)
+    PAR.check_mask(m.cpu().numpy(), ref_s, ref_m, q_start, tau)
+
+
+def test_offloaded_chunked_prefill_streamed_16k():
+    from block_sparse_attention_xattn_amd import synthetic
+    from block_sparse_attention_xattn_amd.offload import OffloadedChunkedPrefill
+    from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
+    w = synthetic.WORKLOADS["llama8b_128k_last_chunk"]
+    q, k, v = synthetic.workload_inputs("llama8b_128k_last_chunk", 16384)
+    p, S, tau = 12288, w["stride"], w["threshold"]
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    off = OffloadedChunkedPrefill(qd, kd, vd, chunk=4096, stride=S, threshold=tau, cache_block=1024, group=4,
+                                  chunk_starts=[p], estimator="streamed")
+    off.run()
+    res = ChunkedPrefill(qd, kd, vd, chunk=4096, stride=S, threshold=tau, chunk_starts=[p], cache_block=1024)
+    res.run()
+    torch.cuda.synchronize()
+    keep_res = [i for i, x in enumerate(res.bufs[0].keep_any.cpu().tolist()) if x]
+    assert off.kept[p] == keep_res
+    rs, rm = O.estimate(_np(q[p:]), _np(k), p, S, tau)
+    ref_keep = O.mask_to_cache_blocks(rm, 0, p // 1024)[1]
+    assert off.kept[p] == [i for i in range(p // 1024) if ref_keep[i]]
     keep = O.expand_cache_keep(ref_keep, 8, p // 128)
     g = w["hq"] // w["hkv"]
     for h, qb in [(0, 0), (13, 17), (31, 31)]:
