@@ -45,6 +45,10 @@ Readings where the pages are open (each is restated where it is used):
 * Estimate against the downsampled history: every history key precedes the
   chunk, so no causal limit applies, and the chunk's diagonal block lies past
   the history keys, so block 0 is the only forced block.
+* Packed batch (``compute_prefill`` handles one sequence and leaves larger
+  batches to dense attention): each sequence is its own problem, its queries
+  at the end of its keys (q_start_pos = k_len - q_len), with no attention
+  across sequences.
 
 All arrays are numpy float64 unless stated; token-major layouts
 ``[tokens, heads, head_dim]`` as in the pages' varlen tensors.
@@ -563,3 +567,47 @@ def history_cache_blocks_downsampled(mask, n_cache_blocks: int, sub_blocks: int 
     mask: [Hq, nQB, n_blocks] -> keep uint8 [n_cache_blocks].
     """
     return mask_to_cache_blocks(mask, 0, n_cache_blocks, sub_blocks, force_first_last=False)[1]
+
+
+# ---------------------------------------------------------------------------
+# Next step: a packed batch of sequences (varlen)
+# ---------------------------------------------------------------------------
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, stride: int, threshold: float, block: int = 128,
+                   softmax_scale=None, rule: str = "greedy"):
+    """GPU-only prefill of a packed batch, one sequence at a time.
+
+    XAttentionBSAPolicy ``compute_prefill``: Q, K, V packed sequence after
+    sequence with cumulative lengths; for a sequence, the estimate of its
+    queries against its keys (causal, queries at the end of the keys:
+    q_start_pos = k_len - q_len), the selection, and block-sparse causal
+    attention with that mask.  The page handles one sequence and falls back
+    to dense attention for more; here every sequence runs the same method
+    on its own rows and keys.
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; cu_seqlens_*: [batch + 1].
+    Returns dict(out [total_q, Hq, d], lse (list of [Hq, q_len_b]),
+    scores, masks (lists of [Hq, q_len_b/block, k_len_b/block])).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    out = np.zeros(q.shape)
+    lses, scores, masks = [], [], []
+    for b in range(len(cq) - 1):
+        qb, kb, vb = q[cq[b]:cq[b + 1]], k[ck[b]:ck[b + 1]], v[ck[b]:ck[b + 1]]
+        p = kb.shape[0] - qb.shape[0]
+        if qb.shape[0] == 0:
+            lses.append(np.zeros((q.shape[1], 0)))
+            scores.append(np.zeros((q.shape[1], 0, kb.shape[0] // block)))
+            masks.append(np.zeros((q.shape[1], 0, kb.shape[0] // block), dtype=np.uint8))
+            continue
+        sc, m = estimate(qb, kb, p, stride, threshold, block, rule)
+        o, lse = bsa(qb, kb, vb, p, 0, m, 0, True, softmax_scale, block)
+        out[cq[b]:cq[b + 1]] = o
+        lses.append(lse)
+        scores.append(sc)
+        masks.append(m)
+    return dict(out=out, lse=lses, scores=scores, masks=masks)
