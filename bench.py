@@ -196,11 +196,145 @@ def cpu_baseline(name, groups, w):
                       f"{sum(times):.1f} s of CPU time"}
 
 
+def varlen_flops(run):
+    """(attention computed-block flops, estimate flops, density) of a packed-batch step from its masks."""
+    import numpy as np
+    d, S, blk = run.d, run.stride, run.block
+    per_tile = 4.0 * d * blk * blk
+    att = est = 0.0
+    sel = tot = 0
+    for b, m in enumerate(run.masks()):
+        ql, kl = run.cu_q[b + 1] - run.cu_q[b], run.cu_k[b + 1] - run.cu_k[b]
+        if ql == 0:
+            continue
+        m = m.cpu().numpy().astype(bool)
+        hq, nqb, nkb = m.shape
+        cur = (kl - ql) // blk
+        causal = np.arange(nkb)[None, :] <= (cur + np.arange(nqb))[:, None]
+        n = int((m & causal[None]).sum())
+        att += per_tile * n
+        sel += n
+        tot += int(causal.sum()) * hq
+        R = ql // S
+        est += 2.0 * d * S * float(np.sum((kl - ql) // S + np.arange(R) + 1)) * hq
+    return att, est, sel / max(tot, 1)
+
+
+def measure_varlen(a, w, q, k, v):
+    """Packed batch: one pack + estimate + attention per step over every sequence; also the same calls made
+    sequence by sequence (single-sequence entry points) on the same inputs, for comparison."""
+    import torch
+    from block_sparse_attention_xattn_amd import binding as B
+    from block_sparse_attention_xattn_amd.varlen import VarlenPrefill
+    cu = [0]
+    for n in w["lengths"]:
+        cu.append(cu[-1] + n)
+    S, tau = w["stride"], w["threshold"]
+    run = VarlenPrefill(q, k, v, cu, cu, S, tau)
+    for _ in range(a.warmup):
+        run.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        run.pack()
+        e[1].record(stream)
+        run.estimate()
+        e[2].record(stream)
+        run.attend()
+        e[3].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
+    est_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+    att_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / a.steps
+    att_f, est_f, dens = varlen_flops(run)
+
+    # the same work as one call per sequence (buffers allocated up front)
+    seqs = []
+    for b in range(len(cu) - 1):
+        n = cu[b + 1] - cu[b]
+        qs, ks, vs = q[cu[b]:cu[b + 1]], k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]]
+        pk = B.PackedV(n, run.hkv, run.d, q.dtype, q.device)
+        nb = n // 128
+        seqs.append(dict(q=qs, k=ks, v=vs, packed=pk,
+                         sc=torch.empty(run.hq, nb, nb, dtype=torch.float32, device=q.device),
+                         m=torch.empty(run.hq, nb, nb, dtype=torch.uint8, device=q.device),
+                         ews=B.workspace(B.xattn_estimate_workspace_size(n, n, run.hq, run.hkv, run.d, S), q.device),
+                         bws=B.workspace(B.bsa_prefill_packed_workspace_size(n, n, run.hq, run.hkv, run.d),
+                                         q.device),
+                         out=torch.empty_like(qs), lse=torch.empty(run.hq, n, dtype=torch.float32, device=q.device)))
+
+    def loop():
+        for x in seqs:
+            B.bsa_pack_v(x["v"], x["packed"], 0)
+            B.xattn_estimate(x["q"], x["k"], 0, S, tau, block_scores=x["sc"], block_mask=x["m"], ws=x["ews"])
+            B.bsa_prefill_packed(x["q"], x["k"], x["packed"], 0, 0, 0, x["m"], 0, True, out=x["out"], lse=x["lse"],
+                                 ws=x["bws"])
+    for _ in range(a.warmup):
+        loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        loop()
+    torch.cuda.synchronize()
+    loop_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    tokens = cu[-1]
+    achieved = att_f / (att_ms * 1e-3) / 1e12
+    return {
+        "metric": "sparse prefill tokens/s per layer (estimate+BSA), packed batch of whole prompts",
+        "value": round(tokens / (step_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "lengths": list(w["lengths"]), "tokens": tokens, "q_heads": run.hq,
+                   "kv_heads": run.hkv, "head_dim": run.d, "stride": S, "threshold": tau, "block": 128},
+        "roofline": {"bound": "mfma", "kernel": "bsa2_kernel<128, bf16> packed-batch form (block-sparse attention)",
+                     "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "timed_call": "one attention call: record upload, work-order kernels, attention, split merge"},
+        "density": round(dens, 4),
+        "parts_ms": {"pack": round(pack_ms, 3), "estimate": round(est_ms, 3), "attention": round(att_ms, 3)},
+        "estimate_gflop": round(est_f / 1e9, 1), "bsa_gflop": round(att_f / 1e9, 1),
+        "per_sequence_calls_ms_per_step": round(loop_ms, 3),
+        "speedup_vs_per_sequence_calls": round(loop_ms / step_ms, 3),
+    }
+
+
+def cpu_baseline_varlen(w, groups):
+    """The oracle's packed-batch prefill on `groups` kv-head groups of every sequence, scaled by the head
+    fraction."""
+    import numpy as np
+    from block_sparse_attention_xattn_amd import synthetic
+    from oracle import xattn_oracle as O
+    q, k, v, cu = synthetic.packed_batch(w["lengths"], w["hq"], w["hkv"], w["d"], w.get("n_needles", 16), w["seed"])
+    g = w["hq"] // w["hkv"]
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    qs, ks, vs = f(q[:, :groups * g]), f(k[:, :groups]), f(v[:, :groups])
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    O.prefill_varlen(qs, ks, vs, cu, cu, w["stride"], w["threshold"])
+    dt = time.perf_counter() - t0
+    frac = groups / w["hkv"]
+    return {"value": round(cu[-1] * frac / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle (prefill_varlen: estimate, selection, causal sparse attention of every "
+                      f"sequence) for {groups} of {w['hkv']} kv-head groups ({groups * g} of {w['hq']} query heads) "
+                      f"of all {len(w['lengths'])} sequences; tokens/s scaled by the head fraction (heads are "
+                      f"independent); {dt:.1f} s of CPU time"}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
-                                   "this build (the path shards by kv-head group, see DESIGN.md)",
+        print(json.dumps({"error": "this benchmark measures exactly one GPU; runs on several GPUs are not "
+                                   "supported (the path shards by kv-head group with no exchange)",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     if a.copy_mib:
@@ -210,6 +344,15 @@ def main():
 
     base = dict(synthetic.WORKLOADS[a.workload])
     q, k, v = (t.to("cuda:0") for t in synthetic.workload_inputs(a.workload))
+    if base.get("varlen"):
+        w = dict(base)
+        w["stride"] = a.stride if a.stride is not None else w["stride"]
+        w["threshold"] = a.threshold if a.threshold is not None else w["threshold"]
+        out = measure_varlen(a, w, q, k, v)
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_varlen(w, a.cpu_groups)
+        print(json.dumps(out))
+        return
     if a.sweep:
         # every (stride, threshold) point of the workload on the same inputs, one line each
         for stride in base.get("strides", (base.get("stride", 8),)):

@@ -86,6 +86,17 @@ def _declare(lib):
                                           I32, P, P, P, P, P, P, P, P]
     lib.xattn_estimate_offloaded.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I32, I32, I64, P,
                                              I64, I32, I32, P, I32, I32, F, P, P, P, SZ, P, P]
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    lib.xattn_varlen_mask_elems.restype = I64
+    lib.xattn_varlen_mask_elems.argtypes = [I64P, I64P, I32, I32]
+    lib.xattn_estimate_varlen_workspace_size.restype = SZ
+    lib.xattn_estimate_varlen_workspace_size.argtypes = [I64P, I64P, I32, I32, I32, I32]
+    lib.xattn_estimate_varlen.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64P, I64P, I32, I32, I32, I32, I32,
+                                          I32, F, P, P, P, SZ, P]
+    lib.bsa_prefill_varlen_workspace_size.restype = SZ
+    lib.bsa_prefill_varlen_workspace_size.argtypes = [I64P, I64P, I32, I32, I32]
+    lib.bsa_prefill_varlen.argtypes = [P, I64, I64, P, I64, I64, P, I64, ctypes.c_int, I64P, I64P, I32, I32, I32, I32,
+                                       P, I32, F, P, ctypes.c_int, P, P, SZ, P]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
@@ -420,6 +431,97 @@ def xattn_estimate_offloaded(q, k_cur, q_start_pos: int, store: OffloadedKV, str
                                           float(threshold), _ptr(block_scores), _ptr(block_mask), _ptr(ws),
                                           ws.numel(), _stream(stream), store.copy_stream.cuda_stream))
     return block_scores, block_mask
+
+
+def _cu(cu):
+    vals = [int(x) for x in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+    return (ctypes.c_int64 * len(vals))(*vals), len(vals) - 1
+
+
+def xattn_varlen_mask_elems(cu_seqlens_q, cu_seqlens_k, num_q_heads: int) -> int:
+    cq, b = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_k)
+    return int(lib().xattn_varlen_mask_elems(cq, ck, b, num_q_heads))
+
+
+def xattn_estimate_varlen_workspace_size(cu_seqlens_q, cu_seqlens_k, num_q_heads, num_kv_heads, stride) -> int:
+    cq, b = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_k)
+    return int(lib().xattn_estimate_varlen_workspace_size(cq, ck, b, num_q_heads, num_kv_heads, stride))
+
+
+def bsa_prefill_varlen_workspace_size(cu_seqlens_q, cu_seqlens_k, num_q_heads, head_dim) -> int:
+    cq, b = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_k)
+    return int(lib().bsa_prefill_varlen_workspace_size(cq, ck, b, num_q_heads, head_dim))
+
+
+def varlen_blocks(flat, cu_seqlens_q, cu_seqlens_k, num_q_heads: int, block: int = 128):
+    """Per-sequence [Hq, q_len/block, k_len/block] views of a packed-batch scores or mask buffer."""
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    out, off = [], 0
+    for b in range(len(cq) - 1):
+        nq, nk = (cq[b + 1] - cq[b]) // block, (ck[b + 1] - ck[b]) // block
+        n = num_q_heads * nq * nk
+        out.append(flat[off:off + n].view(num_q_heads, nq, nk))
+        off += n
+    return out
+
+
+def varlen_lse(flat, cu_seqlens_q, num_q_heads: int):
+    """Per-sequence [Hq, q_len] views of a packed-batch LSE buffer."""
+    cq = [int(x) for x in cu_seqlens_q]
+    return [flat[num_q_heads * cq[b]:num_q_heads * cq[b + 1]].view(num_q_heads, cq[b + 1] - cq[b])
+            for b in range(len(cq) - 1)]
+
+
+def xattn_estimate_varlen(q, k, cu_seqlens_q, cu_seqlens_k, stride: int = 8, threshold: float = 0.9,
+                          block: int = 128, block_scores=None, block_mask=None, ws=None, stream=None):
+    """Estimate of every sequence of a packed batch (see xattn.h).  Returns flat (scores, mask)."""
+    _qkv_check(q, "q")
+    _qkv_check(k, "k")
+    _, hq, d = q.shape
+    hkv = k.shape[1]
+    cq, b = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_k)
+    n = int(lib().xattn_varlen_mask_elems(cq, ck, b, hq))
+    if n < 0:
+        raise XattnError(XA_EINVAL, "invalid packed-batch lengths")
+    if block_scores is None:
+        block_scores = torch.empty(max(n, 1), dtype=torch.float32, device=q.device)
+    if block_mask is None:
+        block_mask = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = workspace(lib().xattn_estimate_varlen_workspace_size(cq, ck, b, hq, hkv, stride), q.device)
+    _check(lib().xattn_estimate_varlen(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+                                       _dtype_code(q), cq, ck, b, hq, hkv, d, stride, block, float(threshold),
+                                       _ptr(block_scores), _ptr(block_mask), _ptr(ws), ws.numel(), _stream(stream)))
+    return block_scores, block_mask
+
+
+def bsa_prefill_varlen(q, k, packed: PackedV, cu_seqlens_q, cu_seqlens_k, block_mask=None, softmax_scale=0.0,
+                       out_dtype=None, block: int = 128, out=None, lse=None, ws=None, stream=None):
+    """Causal block-sparse attention of every sequence of a packed batch (see xattn.h).  Returns (out, flat lse)."""
+    _qkv_check(q, "q")
+    _qkv_check(k, "k")
+    total_q, hq, d = q.shape
+    hkv = k.shape[1]
+    cq, b = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_k)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(total_q, hq, d, dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty(max(hq * total_q, 1), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(lib().bsa_prefill_varlen_workspace_size(cq, ck, b, hq, d), q.device)
+    _check(lib().bsa_prefill_varlen(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+                                    _ptr(packed.buf), packed.capacity, _dtype_code(q), cq, ck, b, hq, hkv, d,
+                                    _ptr(block_mask) if block_mask is not None else None, block,
+                                    float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+                                    ws.numel(), _stream(stream)))
+    return out, lse
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "launchers.h"
 
 namespace xa_host {
@@ -612,4 +614,219 @@ extern "C" xa_status_t bsa_prefill_segments(const void* q, int64_t q_tok, int64_
                          g.mask_row_stride, g.mask_kb_offset, block, g.causal, softmax_scale, g.out, g.lse);
   }
   return run_bsa(fn, segs, n_segments, d, dtype, out_dtype, reinterpret_cast<hipStream_t>(stream), &plan);
+}
+
+// ---------------------------------------------------------------------------
+// Packed batch of sequences (varlen)
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int32_t kMaxBatch = 1 << 16;
+
+struct VarlenShape {
+  std::vector<VarlenSeq> seqs;
+  int64_t n_items = 0;    // attention items = selection workgroups
+  int64_t est_wg = 0;     // estimate-GEMM workgroups
+  int64_t lse_elems = 0;  // estimate partials (floats)
+  int64_t out_elems = 0;  // scores / mask elements
+  int max_nkb = 0;
+  int64_t total_q = 0, total_k = 0;
+};
+
+// Lengths from the host prefix arrays; every length a multiple of 128, each sequence's queries at most
+// its keys.  stride 0: no estimate sizes.
+xa_status_t varlen_shape(const char* fn, const int64_t* cu_q, const int64_t* cu_k, int32_t batch, int32_t hq,
+                         int32_t hkv, int32_t stride, VarlenShape& V) {
+  if (!cu_q || !cu_k) return fail(XA_EINVAL, "%s: cu_seqlens_q and cu_seqlens_k are required", fn);
+  if (batch < 1 || batch > kMaxBatch) return fail(XA_EINVAL, "%s: batch %d outside 1..%d", fn, batch, kMaxBatch);
+  if (cu_q[0] != 0 || cu_k[0] != 0) return fail(XA_EINVAL, "%s: cu_seqlens must start at 0", fn);
+  V.seqs.resize((size_t)batch);
+  const int group = hq / hkv;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t ql = cu_q[b + 1] - cu_q[b], kl = cu_k[b + 1] - cu_k[b];
+    if (ql < 0 || kl < 0 || ql % 128 || kl % 128 || ql > kl)
+      return fail(XA_EINVAL, "%s: sequence %d: q_len %lld and k_len %lld must be multiples of 128 with q_len <= k_len",
+                  fn, b, (long long)ql, (long long)kl);
+    if (kl / 128 > 8192) return fail(XA_EUNSUPPORTED, "%s: sequence %d: more than 8192 key blocks", fn, b);
+    if (cu_q[b + 1] > 0x7fffffff || cu_k[b + 1] > 0x7fffffff)
+      return fail(XA_EUNSUPPORTED, "%s: more than 2^31 - 1 packed tokens", fn);
+    VarlenSeq& s = V.seqs[(size_t)b];
+    s.q0 = (int)cu_q[b];
+    s.q_len = (int)ql;
+    s.k0 = (int)cu_k[b];
+    s.k_len = (int)kl;
+    s.lse_off = V.lse_elems;
+    s.out_off = V.out_elems;
+    if (stride > 0 && ql > 0) {
+      const int64_t R = ql / stride, N = kl / stride;
+      V.est_wg += (int64_t)hkv * ((N + 255) / 256) * ((R + 255) / 256) * group;
+      V.lse_elems += (int64_t)hq * (kl / 128) * R;
+    }
+    V.n_items += (int64_t)hq * (ql / 128);
+    V.out_elems += (int64_t)hq * (ql / 128) * (kl / 128);
+    if (V.est_wg > 0x7fffffff || V.n_items > ((int64_t)1 << 28))
+      return fail(XA_EUNSUPPORTED, "%s: batch too large for one grid", fn);
+    s.est_end = (int)V.est_wg;
+    s.sel_end = (int)V.n_items;
+    if (ql > 0 && kl / 128 > V.max_nkb) V.max_nkb = (int)(kl / 128);
+  }
+  V.total_q = cu_q[batch];
+  V.total_k = cu_k[batch];
+  return XA_OK;
+}
+
+size_t seqs_bytes(int32_t batch) { return align256((size_t)batch * sizeof(VarlenSeq)); }
+}  // namespace
+
+extern "C" int64_t xattn_varlen_mask_elems(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                           int32_t num_q_heads) {
+  VarlenShape V;
+  if (num_q_heads <= 0 ||
+      varlen_shape("xattn_varlen_mask_elems", cu_seqlens_q, cu_seqlens_k, batch, num_q_heads, 1, 0, V) != XA_OK)
+    return -1;
+  return V.out_elems;
+}
+
+extern "C" size_t xattn_estimate_varlen_workspace_size(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                       int32_t stride) {
+  VarlenShape V;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || stride <= 0 || 128 % stride ||
+      varlen_shape("xattn_estimate_varlen_workspace_size", cu_seqlens_q, cu_seqlens_k, batch, num_q_heads,
+                   num_kv_heads, stride, V) != XA_OK)
+    return 0;
+  return seqs_bytes(batch) + align256((size_t)V.lse_elems * sizeof(float));
+}
+
+extern "C" xa_status_t xattn_estimate_varlen(const void* q, int64_t q_tok, int64_t q_head, const void* k,
+                                             int64_t k_tok, int64_t k_head, xa_dtype_t dtype,
+                                             const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                             int32_t hq, int32_t hkv, int32_t d, int32_t stride, int32_t block,
+                                             float threshold, float* block_scores, uint8_t* block_mask,
+                                             void* workspace, size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "xattn_estimate_varlen";
+  xa_status_t st;
+  if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_BF16 || d != 128) return fail(XA_EUNSUPPORTED, "%s: XA_BF16 with head_dim 128 only", fn);
+  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (stride != 2 && stride != 4 && stride != 8 && stride != 16)
+    return fail(XA_EUNSUPPORTED, "%s: stride %d not in {2, 4, 8, 16}", fn, stride);
+  if (!(threshold >= 0.f)) return fail(XA_EINVAL, "%s: threshold must be >= 0", fn);
+  VarlenShape V;
+  if ((st = varlen_shape(fn, cu_seqlens_q, cu_seqlens_k, batch, hq, hkv, stride, V)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "q", q, q_tok, q_head, V.total_q, hq, d, dtype)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "k", k, k_tok, k_head, V.total_k, hkv, d, dtype)) != XA_OK) return st;
+  if (V.out_elems > 0 && (!block_scores || !block_mask))
+    return fail(XA_EINVAL, "%s: block_scores and block_mask are required", fn);
+  const size_t need = seqs_bytes(batch) + align256((size_t)V.lse_elems * sizeof(float));
+  if (!workspace || ws_bytes < need || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need, ws_bytes);
+  if (V.n_items == 0) return XA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  VarlenSeq* seqs = reinterpret_cast<VarlenSeq*>(w);
+  hipError_t e = upload_words(V.seqs.data(), sizeof(VarlenSeq) * V.seqs.size(), seqs, s);
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: record upload failed: %s", fn, hipGetErrorString(e));
+  EstParams p{};
+  p.q_hi = static_cast<const bf16*>(q);
+  p.q_tok = q_tok;
+  p.q_head = q_head;
+  p.k_hi = static_cast<const bf16*>(k);
+  p.k_tok = k_tok;
+  p.k_head = k_head;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.S = stride;
+  p.b = block / stride;
+  p.scale_log2 = kLog2e / ((float)stride * sqrtf((float)d));
+  p.lse_part = reinterpret_cast<float*>(w + seqs_bytes(batch));
+  p.seqs = seqs;
+  p.n_seqs = batch;
+  p.grid_total = (int)V.est_wg;
+  if ((e = launch_est_gemm_varlen(p, s)) != hipSuccess)
+    return fail(XA_EHIP, "%s: estimate GEMM launch failed: %s", fn, hipGetErrorString(e));
+  SelParams sp{};
+  sp.lse_part = p.lse_part;
+  sp.b = p.b;
+  sp.hq = hq;
+  sp.nkb = V.max_nkb;
+  sp.npow_cap = 1;
+  while (sp.npow_cap < sp.nkb) sp.npow_cap <<= 1;
+  sp.threshold = threshold;
+  sp.scores = block_scores;
+  sp.mask = block_mask;
+  sp.seqs = seqs;
+  sp.n_seqs = batch;
+  if ((e = launch_est_select_varlen(sp, (int)V.n_items, s)) != hipSuccess)
+    return fail(XA_EHIP, "%s: selection launch failed: %s", fn, hipGetErrorString(e));
+  return XA_OK;
+}
+
+extern "C" size_t bsa_prefill_varlen_workspace_size(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                                    int32_t batch, int32_t num_q_heads, int32_t head_dim) {
+  VarlenShape V;
+  if (num_q_heads <= 0 || head_dim <= 0 ||
+      varlen_shape("bsa_prefill_varlen_workspace_size", cu_seqlens_q, cu_seqlens_k, batch, num_q_heads, 1, 0, V) !=
+          XA_OK)
+    return 0;
+  return seqs_bytes(batch) + bsa_plan_layout(V.n_items, head_dim).total;
+}
+
+extern "C" xa_status_t bsa_prefill_varlen(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                                          int64_t k_head, const void* packed_v, int64_t capacity, xa_dtype_t dtype,
+                                          const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                          int32_t hq, int32_t hkv, int32_t d, const uint8_t* block_mask,
+                                          int32_t block, float softmax_scale, void* out, xa_dtype_t out_dtype,
+                                          float* lse, void* workspace, size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "bsa_prefill_varlen";
+  xa_status_t st;
+  if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
+  if (dtype != XA_BF16 || d != 128) return fail(XA_EUNSUPPORTED, "%s: XA_BF16 with head_dim 128 only", fn);
+  if (out_dtype != XA_F32 && out_dtype != XA_BF16)
+    return fail(XA_EUNSUPPORTED, "%s: out_dtype must be XA_F32 or XA_BF16", fn);
+  if (block != 128) return fail(XA_EUNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (!(softmax_scale >= 0.f)) return fail(XA_EINVAL, "%s: softmax_scale must be >= 0 (0 = 1/sqrt(d))", fn);
+  VarlenShape V;
+  if ((st = varlen_shape(fn, cu_seqlens_q, cu_seqlens_k, batch, hq, hkv, 0, V)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "q", q, q_tok, q_head, V.total_q, hq, d, dtype)) != XA_OK) return st;
+  if ((st = check_tensor(fn, "k", k, k_tok, k_head, V.total_k, hkv, d, dtype)) != XA_OK) return st;
+  if (!packed_v || (uintptr_t)packed_v % 256 != 0) return fail(XA_EINVAL, "%s: packed_v must be 256-byte aligned", fn);
+  const int64_t pitch = packed_pitch(capacity);
+  if (capacity <= 0 || V.total_k > pitch)
+    return fail(XA_EINVAL, "%s: the %lld packed keys exceed the capacity %lld", fn, (long long)V.total_k,
+                (long long)pitch);
+  if (V.n_items > 0 && (!out || !lse)) return fail(XA_EINVAL, "%s: out and lse are required", fn);
+  if ((uintptr_t)out % 16 != 0) return fail(XA_EINVAL, "%s: out must be 16-byte aligned", fn);
+  if ((127 * k_tok + d) * 2 >= ((int64_t)1 << 32) || ((int64_t)(d - 1) * pitch + 128) * 2 >= ((int64_t)1 << 32))
+    return fail(XA_EUNSUPPORTED, "%s: k stride or packed capacity too large for 32-bit tile offsets", fn);
+  const BsaPlanLayout L = bsa_plan_layout(V.n_items, d);
+  const size_t need = seqs_bytes(batch) + L.total;
+  if (!workspace || ws_bytes < need || (uintptr_t)workspace % 256 != 0)
+    return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need, ws_bytes);
+  if (V.n_items == 0) return XA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  VarlenSeq* seqs = reinterpret_cast<VarlenSeq*>(w);
+  hipError_t e = upload_words(V.seqs.data(), sizeof(VarlenSeq) * V.seqs.size(), seqs, s);
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: record upload failed: %s", fn, hipGetErrorString(e));
+  char* pw = w + seqs_bytes(batch);
+  BsaPlan plan{};
+  plan.ctl = reinterpret_cast<int*>(pw + L.ctl);
+  plan.weights = reinterpret_cast<int*>(pw + L.weights);
+  plan.mid = reinterpret_cast<int*>(pw + L.mid);
+  plan.slot = reinterpret_cast<int*>(pw + L.slot);
+  plan.split_items = reinterpret_cast<int*>(pw + L.split_items);
+  plan.order = reinterpret_cast<int*>(pw + L.order);
+  plan.part_o = reinterpret_cast<float*>(pw + L.part_o);
+  plan.part_lse = reinterpret_cast<float*>(pw + L.part_lse);
+  plan.max_split = L.max_split;
+  plan.slots = resident_workgroups();
+  // shared fields; each sequence's rows, lengths, mask block and outputs are taken relative to them
+  const BsaParams shared = bsa_params(static_cast<const bf16*>(q), q_tok, q_head, nullptr, static_cast<const bf16*>(k),
+                                      k_tok, k_head, nullptr, static_cast<const bf16*>(packed_v), nullptr, pitch, 128,
+                                      128, hq, hkv, d, 0, 0, block_mask, 0, 0, 0, block, 1, softmax_scale, out, lse);
+  e = out_dtype == XA_BF16 ? launch_bsa_varlen<bf16>(shared, seqs, batch, (int)V.n_items, &plan, s)
+                           : launch_bsa_varlen<float>(shared, seqs, batch, (int)V.n_items, &plan, s);
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: attention launch failed: %s", fn, hipGetErrorString(e));
+  return XA_OK;
 }

@@ -23,6 +23,10 @@
 //   * the walk over key blocks touches only kept blocks, in ascending order,
 //     from a list built in LDS from the mask row.
 // XA_F32 inputs use bf16 hi/lo planes and three MFMAs per product.
+#include <string.h>
+
+#include <vector>
+
 #include "launchers.h"
 
 namespace xa {
@@ -389,14 +393,69 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// Segment of work item `item` (kernel-argument segments) and the first item of that segment.
+__device__ __forceinline__ const BsaParams& find_seg(const BsaMulti& M, int item, int& item0) {
+  int sidx = 0;
+  while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
+  item0 = sidx ? M.wg_end[sidx - 1] : 0;
+  return M.seg[sidx];
+}
+
+__device__ __forceinline__ int64_t rfl64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Packed batch: the sequence of work item `item` (binary search of the records' item prefix ends,
+// uniform per workgroup) and its problem, seg[0]'s shared fields taken relative to the sequence: its
+// query / key / packed-V rows, causal with the queries at the end of its keys, its compact block mask
+// [hq][q_len/128][k_len/128], its output rows and its LSE block [hq][q_len].
 template <int D, typename OutT>
+__device__ __forceinline__ BsaParams varlen_params(const BsaMulti& M, int item, int& item0) {
+  int lo = 0, hi = M.n_seg - 1;
+  while (lo < hi) {
+    const int md = (lo + hi) >> 1;
+    if (item < __builtin_amdgcn_readfirstlane(M.seqs[md].sel_end)) hi = md;
+    else lo = md + 1;
+  }
+  item0 = lo ? __builtin_amdgcn_readfirstlane(M.seqs[lo - 1].sel_end) : 0;
+  const VarlenSeq& v = M.seqs[lo];
+  const int q0 = __builtin_amdgcn_readfirstlane(v.q0);
+  const int ql = __builtin_amdgcn_readfirstlane(v.q_len);
+  const int k0 = __builtin_amdgcn_readfirstlane(v.k0);
+  const int kl = __builtin_amdgcn_readfirstlane(v.k_len);
+  BsaParams P = M.seg[0];
+  P.q_hi += (int64_t)q0 * P.q_tok;
+  P.k_hi += (int64_t)k0 * P.k_tok;
+  P.vt_hi += k0;
+  P.q_len = ql;
+  P.kv_len = kl;
+  P.n_qb = ql / kBlk;
+  P.q_start = kl - ql;
+  P.kv_start = 0;
+  if (P.mask) {
+    P.mask += rfl64(v.out_off);
+    P.mask_rs = kl / kBlk;
+    P.mask_hs = (int64_t)(ql / kBlk) * (kl / kBlk);
+    P.mask_off = 0;
+  }
+  P.out = static_cast<OutT*>(P.out) + (int64_t)q0 * P.hq * D;
+  P.lse += (int64_t)P.hq * q0;
+  return P;
+}
+
+template <int D, typename OutT>
+__device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid);
+
+template <int D, typename OutT, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
   __shared__ int s_item;
   int item = (int)blockIdx.x, part = 0;
   if (M.order) {
     // the grid has room for every possible split; only items + splits workgroups take a ticket
     // (the split count is read only by the workgroups past the item count)
-    const int n_items = M.wg_end[M.n_seg - 1];
+    const int n_items = M.n_items;
     if ((int)blockIdx.x >= n_items && (int)blockIdx.x >= n_items + M.ctl[2]) return;
     if (threadIdx.x == 0) {
       const int t = atomicAdd(&M.ctl[0], 1);
@@ -408,10 +467,18 @@ __global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
     item = e >> 2;
     part = e & 3;
   }
-  int sidx = 0;
-  while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
-  const BsaParams& P = M.seg[sidx];
-  const int bid = item - (sidx ? M.wg_end[sidx - 1] : 0);
+  int item0;
+  if constexpr (VARLEN) {
+    const BsaParams P = varlen_params<D, OutT>(M, item, item0);
+    bsa2_body<D, OutT>(M, P, item, part, item - item0);
+  } else {
+    const BsaParams& P = find_seg(M, item, item0);
+    bsa2_body<D, OutT>(M, P, item, part, item - item0);
+  }
+}
+
+template <int D, typename OutT>
+__device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid) {
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
   constexpr int KTB = 128 * KCH * 16;     // K tile bytes
   constexpr int VTB = D * 256;            // V^T tile bytes (D rows x 128 keys)
@@ -753,30 +820,33 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
 constexpr int kPlanBins = 4096;  // counts >= kPlanBins-1 share the last bin
 constexpr int kMinSplit = 32;    // items with fewer kept tiles are never split
 
-__device__ __forceinline__ void item_span(const BsaMulti& M, int item, int& sidx, int& h, int& qb, int64_t& jb_end) {
-  sidx = 0;
-  while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
-  const BsaParams& P = M.seg[sidx];
-  bsa_decode(item - (sidx ? M.wg_end[sidx - 1] : 0), P.group, P.hkv, P.n_qb, h, qb);
+template <int D, typename OutT, bool VARLEN>
+__device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int& h, int& qb, int64_t& jb_end) {
+  int item0;
+  BsaParams P;
+  if constexpr (VARLEN) P = varlen_params<D, OutT>(M, item, item0);
+  else P = find_seg(M, item, item0);
+  bsa_decode(item - item0, P.group, P.hkv, P.n_qb, h, qb);
   const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
   jb_end = nkb;
   if (P.causal) {
     const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
     jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
   }
+  return P;
 }
 
 // One wave per work item: kept key blocks below the causal limit, and the key
 // block of its (count / 2)-th kept block (0-based), where a second half starts.
+template <bool VARLEN>
 __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items, int* __restrict__ weights,
                                                          int* __restrict__ mid) {
   const int item = (int)blockIdx.x * 4 + wave_id();
   const int lane = lane_id();
   if (item >= n_items) return;
-  int sidx, h, qb;
+  int h, qb;
   int64_t jb_end;
-  item_span(M, item, sidx, h, qb, jb_end);
-  const BsaParams& P = M.seg[sidx];
+  const BsaParams P = item_span<128, bf16, VARLEN>(M, item, h, qb, jb_end);
   int cnt;
   int64_t half_at;
   if (P.mask == nullptr) {
@@ -920,13 +990,12 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
 
 // LSE merge of the two halves of split item k (partial slot k) into its
 // segment's out and lse (both -inf: out 0, lse -inf).
-template <int D, typename OutT>
+template <int D, typename OutT, bool VARLEN>
 __device__ void split_merge_one(const BsaMulti& M, int k) {
   const int item = M.split_items[k];
-  int sidx, h, qb;
+  int h, qb;
   int64_t jb_end;
-  item_span(M, item, sidx, h, qb, jb_end);
-  const BsaParams& P = M.seg[sidx];
+  const BsaParams P = item_span<D, OutT, VARLEN>(M, item, h, qb, jb_end);
   const float* la = M.part_lse + (size_t)(2 * k) * kBlk;
   const float* lb = la + kBlk;
   const float* oa = M.part_o + (size_t)(2 * k) * kBlk * D;
@@ -964,9 +1033,30 @@ __device__ void split_merge_one(const BsaMulti& M, int k) {
 }
 
 // Split halves are merged by a small grid that strides over the slots in use.
-template <int D, typename OutT>
+template <int D, typename OutT, bool VARLEN>
 __global__ __launch_bounds__(256) void split_merge_kernel(BsaMulti M) {
-  for (int k = (int)blockIdx.x; k < M.ctl[2]; k += (int)gridDim.x) split_merge_one<D, OutT>(M, k);
+  for (int k = (int)blockIdx.x; k < M.ctl[2]; k += (int)gridDim.x) split_merge_one<D, OutT, VARLEN>(M, k);
+}
+
+// Host tables reach device memory through the arguments of a small kernel, in stream order.
+constexpr int kBlobWords = 384;
+struct Blob {
+  uint32_t w[kBlobWords];
+};
+__global__ __launch_bounds__(256) void upload_kernel(Blob b, int n_words, uint32_t* __restrict__ dst) {
+  for (int i = (int)threadIdx.x; i < n_words; i += 256) dst[i] = b.w[i];
+}
+
+hipError_t upload_words(const void* src, size_t bytes, void* dst, hipStream_t s) {
+  if (bytes % 4 != 0) return hipErrorInvalidValue;
+  const size_t words = bytes / 4;
+  for (size_t w0 = 0; w0 < words; w0 += kBlobWords) {
+    const int n = (int)(words - w0 < (size_t)kBlobWords ? words - w0 : (size_t)kBlobWords);
+    Blob b{};
+    memcpy(b.w, static_cast<const uint32_t*>(src) + w0, (size_t)n * 4);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, b, n, static_cast<uint32_t*>(dst) + w0);
+  }
+  return hipGetLastError();
 }
 
 // Explicit instantiation helpers used by the ABI layer.
@@ -991,11 +1081,12 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
         m.wg_end[i] = total;
       }
       m.n_seg = n_seg;
+      m.n_items = total;
       if (total > 0) {
         int grid = total;
         if (plan) {
-          hipLaunchKernelGGL(plan_count_kernel, dim3((total + 3) / 4), dim3(256), 0, s, m, total, plan->weights,
-                             plan->mid);
+          hipLaunchKernelGGL(plan_count_kernel<false>, dim3((total + 3) / 4), dim3(256), 0, s, m, total,
+                             plan->weights, plan->mid);
           hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
                              plan->order, plan->ctl, plan->slot, plan->split_items, plan->max_split, plan->slots);
           m.order = plan->order;
@@ -1007,9 +1098,10 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
           m.part_lse = plan->part_lse;
           grid = total + plan->max_split;  // entries: items plus halves of split items
         }
-        hipLaunchKernelGGL((bsa2_kernel<D, OutT>), dim3(grid), dim3(256), 0, s, m);
+        hipLaunchKernelGGL((bsa2_kernel<D, OutT, false>), dim3(grid), dim3(256), 0, s, m);
         if (plan && plan->max_split > 0)
-          hipLaunchKernelGGL((split_merge_kernel<D, OutT>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
+          hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(plan->max_split, 64)), dim3(256), 0, s,
+                             m);
       }
       return hipGetLastError();
     }
@@ -1018,6 +1110,37 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
     hipLaunchKernelGGL((bsa_kernel<D, SPLIT, OutT>), dim3(segs[i].hq * segs[i].n_qb), dim3(kThreads), 0, s, segs[i]);
   return hipGetLastError();
 }
+
+template <typename OutT>
+hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int n_seqs, int n_items,
+                             const BsaPlan* plan, hipStream_t s) {
+  if (n_seqs <= 0 || !plan || !tile_offsets_fit(&shared, 1, 128)) return hipErrorInvalidValue;
+  if (n_items == 0) return hipSuccess;
+  BsaMulti m{};
+  m.seg[0] = shared;
+  m.n_seg = n_seqs;
+  m.n_items = n_items;
+  m.seqs = seqs;
+  hipLaunchKernelGGL(plan_count_kernel<true>, dim3((n_items + 3) / 4), dim3(256), 0, s, m, n_items, plan->weights,
+                     plan->mid);
+  hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, n_items, (const int*)plan->weights, plan->order,
+                     plan->ctl, plan->slot, plan->split_items, plan->max_split, plan->slots);
+  m.order = plan->order;
+  m.ctl = plan->ctl;
+  m.mid = plan->mid;
+  m.slot = plan->slot;
+  m.split_items = plan->split_items;
+  m.part_o = plan->part_o;
+  m.part_lse = plan->part_lse;
+  hipLaunchKernelGGL((bsa2_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(256), 0, s, m);
+  if (plan->max_split > 0)
+    hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+template hipError_t launch_bsa_varlen<bf16>(const BsaParams&, const VarlenSeq*, int, int, const BsaPlan*,
+                                            hipStream_t);
+template hipError_t launch_bsa_varlen<float>(const BsaParams&, const VarlenSeq*, int, int, const BsaPlan*,
+                                             hipStream_t);
 
 template hipError_t launch_bsa<64, false, bf16>(const BsaParams*, int, const BsaPlan*, hipStream_t);
 template hipError_t launch_bsa<64, false, float>(const BsaParams*, int, const BsaPlan*, hipStream_t);

@@ -169,8 +169,36 @@ __device__ __forceinline__ void est_g2lds16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Sequence of packed-batch workgroup w (binary search of the prefix ends, uniform per workgroup); w
+// becomes the workgroup's index inside its sequence.  Record fields go through readfirstlane so they
+// stay in scalar registers.
+template <bool SEL>
+__device__ __forceinline__ const VarlenSeq& varlen_seq(const VarlenSeq* seqs, int n, int& w, int& q0, int& ql,
+                                                       int& k0, int& kl) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int md = (lo + hi) >> 1;
+    const int end = __builtin_amdgcn_readfirstlane(SEL ? seqs[md].sel_end : seqs[md].est_end);
+    if (w < end) hi = md;
+    else lo = md + 1;
+  }
+  if (lo) w -= __builtin_amdgcn_readfirstlane(SEL ? seqs[lo - 1].sel_end : seqs[lo - 1].est_end);
+  const VarlenSeq& v = seqs[lo];
+  q0 = __builtin_amdgcn_readfirstlane(v.q0);
+  ql = __builtin_amdgcn_readfirstlane(v.q_len);
+  k0 = __builtin_amdgcn_readfirstlane(v.k0);
+  kl = __builtin_amdgcn_readfirstlane(v.k_len);
+  return v;
+}
+
+__device__ __forceinline__ int64_t rfl64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <int HALF>
-__global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
+__device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
   constexpr int TILE = 256;
   constexpr int SLICE_B = TILE * 128;      // one operand slice: 256 rows x 64 bf16
   constexpr int BUF_B = 2 * SLICE_B;       // Q slice + K slice
@@ -185,8 +213,6 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
 
   const int n_rt = (P.R + TILE - 1) / TILE;
   const int n_ct = (P.N + TILE - 1) / TILE;
-  const int total = P.hkv * n_ct * n_rt * P.group;
-  int w = xcd_remap(blockIdx.x, total);
   const int j = w % P.group;
   w /= P.group;
   const int rt = w % n_rt;
@@ -292,6 +318,30 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
   }
 }
 
+template <int HALF, bool VARLEN>
+__global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P0) {
+  if constexpr (VARLEN) {
+    int w = xcd_remap(blockIdx.x, P0.grid_total);
+    int q0, ql, k0, kl;
+    const VarlenSeq& v = varlen_seq<false>(P0.seqs, P0.n_seqs, w, q0, ql, k0, kl);
+    EstParams P = P0;
+    P.q_hi += (int64_t)q0 * P.q_tok;
+    P.k_hi += (int64_t)k0 * P.k_tok;
+    P.q_len = ql;
+    P.k_len = kl;
+    P.q_start = kl - ql;
+    P.R = ql / P.S;
+    P.N = kl / P.S;
+    P.nkb = kl / 128;
+    P.nkb_ld = P.nkb;
+    P.lse_part += rfl64(v.lse_off);
+    est_gemm2_body<HALF>(P, w);
+  } else {
+    const int n_rt = (P0.R + 255) / 256, n_ct = (P0.N + 255) / 256;
+    est_gemm2_body<HALF>(P0, xcd_remap(blockIdx.x, P0.hkv * n_ct * n_rt * P0.group));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Block sums + cumulative-threshold selection, one workgroup per
 // (head, query block).
@@ -301,7 +351,7 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P) {
 // B = rows of a query block in the reshaped score matrix (block / stride); the
 // per-row loads are unrolled so that each thread's loads are in flight together.
 template <int B>
-__global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
+__device__ __forceinline__ void est_select_body(const SelParams& P, int w) {
   // dynamic LDS: npow_cap sort keys, then nkb mask bytes
   extern __shared__ __attribute__((aligned(16))) unsigned long long sel_dyn[];
   unsigned long long* keys = sel_dyn;
@@ -314,8 +364,8 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
   __shared__ float s_a0, s_ad;
 
   const int tid = threadIdx.x;
-  const int h = blockIdx.x / P.n_qb;
-  const int qb = blockIdx.x % P.n_qb;
+  const int h = w / P.n_qb;
+  const int qb = w % P.n_qb;
   constexpr int b = B;
   // always-kept diagonal block; key blocks 0..diag visible (history only: all, no diagonal)
   const int64_t diag = P.hist_only ? -1 : P.cur + qb;
@@ -459,16 +509,40 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P) {
   for (int kb = tid; kb < P.nkb; kb += 256) out[kb] = mrow[kb];
 }
 
+template <int B, bool VARLEN>
+__global__ __launch_bounds__(256) void est_select_kernel(SelParams P0) {
+  if constexpr (VARLEN) {
+    int w = (int)blockIdx.x;
+    int q0, ql, k0, kl;
+    const VarlenSeq& v = varlen_seq<true>(P0.seqs, P0.n_seqs, w, q0, ql, k0, kl);
+    SelParams P = P0;
+    P.lse_part += rfl64(v.lse_off);
+    const int64_t oo = rfl64(v.out_off);
+    P.scores += oo;
+    P.mask += oo;
+    P.R = ql / (128 / B);
+    P.nkb = kl / 128;
+    P.n_qb = ql / 128;
+    P.cur = (kl - ql) / 128;
+    int np = 1;
+    while (np < P.nkb) np <<= 1;
+    P.npow_cap = np;
+    est_select_body<B>(P, w);
+  } else {
+    est_select_body<B>(P0, (int)blockIdx.x);
+  }
+}
+
 template <int D, bool SPLIT>
 hipError_t launch_est_gemm(const EstParams& p, hipStream_t s) {
   if constexpr (D == 128 && !SPLIT) {
     const int n_rt = (p.R + 255) / 256, n_ct = (p.N + 255) / 256;
     const int grid = p.hkv * n_ct * n_rt * p.group;
     switch (p.b) {
-      case 8: hipLaunchKernelGGL((est_gemm2_kernel<4>), dim3(grid), dim3(1024), 0, s, p); break;
-      case 16: hipLaunchKernelGGL((est_gemm2_kernel<8>), dim3(grid), dim3(1024), 0, s, p); break;
-      case 32: hipLaunchKernelGGL((est_gemm2_kernel<16>), dim3(grid), dim3(1024), 0, s, p); break;
-      case 64: hipLaunchKernelGGL((est_gemm2_kernel<32>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 8: hipLaunchKernelGGL((est_gemm2_kernel<4, false>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 16: hipLaunchKernelGGL((est_gemm2_kernel<8, false>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 32: hipLaunchKernelGGL((est_gemm2_kernel<16, false>), dim3(grid), dim3(1024), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((est_gemm2_kernel<32, false>), dim3(grid), dim3(1024), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -521,18 +595,38 @@ hipError_t launch_downsample_keys(const void* k, xa_dtype_t dt, int64_t k_tok, i
   return hipGetLastError();
 }
 
-hipError_t launch_est_select(const SelParams& p, hipStream_t s) {
-  const dim3 grid(p.hq * p.n_qb);
+template <bool VARLEN>
+static hipError_t select_launch(const SelParams& p, int grid, hipStream_t s) {
   const size_t lds = (size_t)p.npow_cap * 8 + ((size_t)p.nkb + 15) / 16 * 16;
   auto go = [&](auto kern) {
     if (lds > 65536) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   };
   switch (p.b) {
-    case 8: go(est_select_kernel<8>); break;
-    case 16: go(est_select_kernel<16>); break;
-    case 32: go(est_select_kernel<32>); break;
-    case 64: go(est_select_kernel<64>); break;
+    case 8: go(est_select_kernel<8, VARLEN>); break;
+    case 16: go(est_select_kernel<16, VARLEN>); break;
+    case 32: go(est_select_kernel<32, VARLEN>); break;
+    case 64: go(est_select_kernel<64, VARLEN>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_est_select(const SelParams& p, hipStream_t s) { return select_launch<false>(p, p.hq * p.n_qb, s); }
+
+hipError_t launch_est_select_varlen(const SelParams& p0, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  return select_launch<true>(p0, grid, s);
+}
+
+hipError_t launch_est_gemm_varlen(const EstParams& p0, hipStream_t s) {
+  if (p0.grid_total <= 0) return hipSuccess;
+  const dim3 grid(p0.grid_total);
+  switch (p0.b) {
+    case 8: hipLaunchKernelGGL((est_gemm2_kernel<4, true>), grid, dim3(1024), 0, s, p0); break;
+    case 16: hipLaunchKernelGGL((est_gemm2_kernel<8, true>), grid, dim3(1024), 0, s, p0); break;
+    case 32: hipLaunchKernelGGL((est_gemm2_kernel<16, true>), grid, dim3(1024), 0, s, p0); break;
+    case 64: hipLaunchKernelGGL((est_gemm2_kernel<32, true>), grid, dim3(1024), 0, s, p0); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -6,6 +6,17 @@
 namespace xa {
 
 // Block-sparse attention (bsa.hip).
+// One sequence of a packed batch: rows [q0, q0 + q_len) of q and [k0, k0 + k_len) of k, the query rows
+// at the end of their keys (global positions k_len - q_len ..); est_end / sel_end: prefix ends of the
+// estimate-GEMM and selection workgroups of this and the earlier sequences; lse_off: float offset of its
+// estimate partials [hq][k_len/128][q_len/S]; out_off: element offset of its scores / mask
+// [hq][q_len/128][k_len/128].
+struct VarlenSeq {
+  int q0, q_len, k0, k_len;
+  int est_end, sel_end;
+  int64_t lse_off, out_off;
+};
+
 struct BsaParams {
   const bf16* q_hi;
   const bf16* q_lo;
@@ -42,6 +53,10 @@ struct EstParams {
   int64_t c0;
   int kb0, nkb_ld;
   float* lse_part;  // [hq][nkb_ld][R], log2 units; this call writes key blocks kb0 .. kb0 + nkb - 1
+  // packed batch: workgroup w runs sequence s with seqs[s-1].est_end <= w < seqs[s].est_end, the
+  // pointers, lengths and offsets above taken relative to that sequence
+  const VarlenSeq* seqs;
+  int n_seqs, grid_total;
 };
 
 // Block sums + threshold selection (estimate.hip).
@@ -54,6 +69,9 @@ struct SelParams {
   float threshold;
   float* scores;  // [hq][n_qb][nkb]
   uint8_t* mask;  // [hq][n_qb][nkb]
+  // packed batch, as for EstParams (sel_end: hq * q_len/128 workgroups per sequence)
+  const VarlenSeq* seqs;
+  int n_seqs;
 };
 
 // Up to kMaxSegments attention problems sharing Q, heads and packed V, run as
@@ -70,6 +88,8 @@ struct BsaMulti {
   BsaParams seg[kMaxSegments];
   int wg_end[kMaxSegments];
   int n_seg;
+  int n_items;             // work items of all segments
+  const VarlenSeq* seqs;   // packed batch: n_seg sequences (device memory), seg[0] holds the shared fields
   const int* order;        // entries, longest first (null: no order)
   int* ctl;                // [0] next ticket, [1] entries, [2] split items
   const int* mid;          // [items] first key block (segment-relative) of a split item's second half
@@ -117,6 +137,14 @@ inline BsaPlanLayout bsa_plan_layout(int64_t n_items, int d) {
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s);
+// A packed batch of bf16, head_dim 128 sequences (records seqs in device memory, n_items = hq * total
+// query blocks) as one grid with a work order; `shared` holds the batch's base pointers, strides, heads,
+// scale and the mask base (null: dense causal).  hipErrorInvalidValue when tile offsets do not fit 32 bits.
+template <typename OutT>
+hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int n_seqs, int n_items,
+                             const BsaPlan* plan, hipStream_t s);
+// Copy `bytes` (a multiple of 4) of host memory to device memory in stream order through kernel arguments.
+hipError_t upload_words(const void* src, size_t bytes, void* dst, hipStream_t s);
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv, int D,
                      bf16* vt_hi, bf16* vt_lo, int64_t pitch, int64_t token_offset, hipStream_t s);
 hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, int H, int D, bf16* hi, bf16* lo,
@@ -124,6 +152,10 @@ hipError_t launch_split(const float* x, int64_t tok, int64_t head, int64_t L, in
 template <int D, bool SPLIT>
 hipError_t launch_est_gemm(const EstParams& p, hipStream_t s);
 hipError_t launch_est_select(const SelParams& p, hipStream_t s);
+// Packed-batch forms (bf16, head_dim 128): p0 holds the shared fields, seqs / n_seqs (device memory), the
+// grid total and, for the selection, the largest npow_cap / nkb over the batch (LDS size).
+hipError_t launch_est_gemm_varlen(const EstParams& p0, hipStream_t s);
+hipError_t launch_est_select_varlen(const SelParams& p0, int grid, hipStream_t s);
 hipError_t launch_downsample_keys(const void* k, xa_dtype_t dt, int64_t k_tok, int64_t k_head, int64_t n_out, int hkv,
                                   int d, int stride, void* out, int64_t out_off, hipStream_t s);
 

@@ -93,6 +93,24 @@ def long_context(L: int, hq: int, hkv: int, d: int = 128, n_needles: int = 16,
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
+def packed_batch(lengths, hq: int, hkv: int, d: int = 128, n_needles: int = 16, seed: int = 6):
+    """A packed batch of whole prompts: sequence i is ``long_context(lengths[i], ..., seed + i)``.
+
+    Returns Q [total, hq, d], K, V [total, hkv, d] (sequences one after the other) and the cumulative
+    lengths [batch + 1] (the same for queries and keys).
+    """
+    qs, ks, vs = [], [], []
+    for i, n in enumerate(lengths):
+        q, k, v = long_context(n, hq, hkv, d, n_needles, seed + i)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    return torch.cat(qs), torch.cat(ks), torch.cat(vs), cu
+
+
 # Named workloads (token counts, heads, head_dim, chunking, estimate settings).
 WORKLOADS = {
     "tiny_1k_fp32": dict(L=1024, hq=2, hkv=1, d=64, chunk=1024, stride=8, threshold=0.9,
@@ -107,12 +125,19 @@ WORKLOADS = {
                               dtype="bf16", seed=4, n_needles=16),
     "gqa7_128k_32x4k": dict(L=131072, hq=28, hkv=4, d=128, chunk=4096, stride=8,
                             threshold=0.9, dtype="bf16", seed=5, n_needles=64),
+    # packed batch of whole prompts (GPU-only prefill of several sequences at once)
+    "llama8b_varlen_8seq": dict(lengths=(16384, 12288, 8192, 4096, 4096, 2048, 1024, 1024), hq=32, hkv=8,
+                                d=128, stride=8, threshold=0.95, dtype="bf16", seed=6, n_needles=16,
+                                varlen=True),
 }
 
 
 def workload_inputs(name: str, L: int | None = None):
     """Q, K, V for a named workload (optionally truncated to the first L tokens)."""
     w = WORKLOADS[name]
+    if w.get("varlen"):
+        q, k, v, _ = packed_batch(w["lengths"], w["hq"], w["hkv"], w["d"], w.get("n_needles", 16), w["seed"])
+        return q, k, v
     if w["dtype"] == "f32":
         return tiny(w["seed"], w["L"], w["hq"], w["hkv"], w["d"])
     n = w["L"] if L is None else L

@@ -364,6 +364,63 @@ xa_status_t xattn_estimate_offloaded(const void* q, int64_t q_tok_stride, int64_
                                      xa_stream_t copy_stream);
 
 /* ------------------------------------------------------------------------
+ * Packed batch of sequences (varlen)
+ *
+ * XAttentionBSAPolicy page, compute_prefill (GPU-only mode): Q [total_q][heads][d] and
+ * K / V [total_kv][kv_heads][d] packed sequence after sequence, with
+ * cumulative lengths cu_seqlens_q / cu_seqlens_k [batch + 1]; the page runs
+ * the estimate and the block-sparse attention for one sequence and leaves
+ * batches above one to dense attention.  Here sequence b is its own
+ * problem: queries rows cu_q[b] .. cu_q[b+1]-1 at global positions
+ * k_len_b - q_len_b .. (the queries end where the keys end), keys rows
+ * cu_k[b] .. cu_k[b+1]-1, causal; every sequence of the batch runs in one
+ * grid per kernel (one estimate GEMM, one selection, one attention with a
+ * work order across all sequences).
+ *
+ * cu_seqlens_q / cu_seqlens_k: HOST arrays of batch + 1 int64, starting at
+ * 0, non-decreasing; every q_len_b and k_len_b a multiple of 128 with
+ * q_len_b <= k_len_b (a sequence with q_len_b = 0 contributes nothing);
+ * 1 <= batch <= 65536; at most 8192 key blocks per sequence.  bf16 inputs,
+ * head_dim 128.
+ *
+ * Scores / mask of a batch: sequence b's [num_q_heads][q_len_b/128]
+ * [k_len_b/128] block after those of sequences 0..b-1 (element offset the
+ * sum of the earlier blocks; xattn_varlen_mask_elems gives the total, -1 on
+ * invalid lengths).  Out: [total_q][num_q_heads][head_dim] rows as q.  LSE:
+ * sequence b's [num_q_heads][q_len_b] block at float offset num_q_heads *
+ * cu_q[b].
+ *
+ * xattn_estimate_varlen: xattn_estimate of every sequence (its q_start_pos =
+ *   k_len_b - q_len_b), stride in {2, 4, 8, 16}, block 128; workspace of
+ *   xattn_estimate_varlen_workspace_size bytes (256-byte aligned): the
+ *   sequence records and the per-(row, key block) LSE partials.
+ * bsa_prefill_varlen: bsa_prefill of every sequence with its mask block
+ *   (block_mask null: dense causal); packed_v holds the batch's V packed by
+ *   bsa_pack_v as tokens 0 .. total_kv - 1 (capacity >= total_kv); workspace
+ *   of bsa_prefill_varlen_workspace_size bytes (records and work order).
+ * Errors as for the single-sequence calls; nothing is queued on an error.
+ * ------------------------------------------------------------------------ */
+int64_t xattn_varlen_mask_elems(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                int32_t num_q_heads);
+size_t xattn_estimate_varlen_workspace_size(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                            int32_t num_q_heads, int32_t num_kv_heads, int32_t stride);
+xa_status_t xattn_estimate_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride, const void* k,
+                                  int64_t k_tok_stride, int64_t k_head_stride, xa_dtype_t dtype,
+                                  const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t stride,
+                                  int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
+                                  void* workspace, size_t workspace_bytes, xa_stream_t stream);
+size_t bsa_prefill_varlen_workspace_size(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k, int32_t batch,
+                                         int32_t num_q_heads, int32_t head_dim);
+xa_status_t bsa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride, const void* k,
+                               int64_t k_tok_stride, int64_t k_head_stride, const void* packed_v, int64_t capacity,
+                               xa_dtype_t dtype, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               const uint8_t* block_mask, int32_t block, float softmax_scale, void* out,
+                               xa_dtype_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                               xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Part 3: LSE merge  (merge_attention_outputs)
  *
  * nano-vllm CLAUDE.md, "Online Softmax Merge - Triton Fused Kernel":

@@ -212,3 +212,37 @@ def test_offload_entry_points_reject(lib):
     assert est(ws=ctypes.c_void_p(0x100010)) == B.XA_EWORKSPACE
     assert est(tau=float("nan")) == B.XA_EINVAL
     assert est(dt=B.XA_F32) == B.XA_EUNSUPPORTED
+
+
+def test_varlen_sizes_and_rejects(lib):
+    C = lambda xs: (ctypes.c_int64 * len(xs))(*xs)  # noqa: E731
+    cq, ck = [0, 256, 256, 640], [0, 512, 768, 1664]            # lens (256, 512), (0, 256), (384, 896)
+    assert B.xattn_varlen_mask_elems(cq, ck, 4) == 4 * (2 * 4 + 0 + 3 * 7)
+    assert B.xattn_varlen_mask_elems([0, 100], [0, 128], 4) == -1            # ragged
+    assert B.xattn_varlen_mask_elems([0, 256], [0, 128], 4) == -1            # q_len > k_len
+    assert B.xattn_varlen_mask_elems([128, 256], [0, 256], 4) == -1          # not starting at 0
+    lse_floats = 4 * (4 * 256 // 8 + 0 + 7 * 384 // 8)
+    assert B.xattn_estimate_varlen_workspace_size(cq, ck, 4, 2, 8) == 256 + (lse_floats * 4 + 255) // 256 * 256
+    assert B.bsa_prefill_varlen_workspace_size(cq, ck, 4, 128) == 256 + _plan_bytes(4 * (2 + 0 + 3), 128)
+    need_e = B.xattn_estimate_varlen_workspace_size(cq, ck, 4, 2, 8)
+
+    def est(cq=cq, ck=ck, b=3, d=128, S=8, ws=FAKE, wsb=need_e, dt=B.XA_BF16):
+        return lib.xattn_estimate_varlen(FAKE, 512, 128, FAKE2, 256, 128, dt, C(cq), C(ck), b, 4, 2, d, S, 128, 0.9,
+                                         FAKE, FAKE2, ws, wsb, None)
+    assert est(d=64) == B.XA_EUNSUPPORTED
+    assert est(dt=B.XA_F32) == B.XA_EUNSUPPORTED
+    assert est(S=3) == B.XA_EUNSUPPORTED
+    assert est(cq=[0, 256, 256, 700]) == B.XA_EINVAL
+    assert est(ck=[0, 128, 384, 1280]) == B.XA_EINVAL                     # first sequence: q_len > k_len
+    assert est(b=0) == B.XA_EINVAL
+    assert est(wsb=need_e - 1) == B.XA_EWORKSPACE
+    need_b = B.bsa_prefill_varlen_workspace_size(cq, ck, 4, 128)
+
+    def bsa(cap=1664, out=FAKE, odt=B.XA_BF16, ws=FAKE2, wsb=need_b, d=128):
+        return lib.bsa_prefill_varlen(FAKE, 512, 128, FAKE2, 256, 128, FAKE, cap, B.XA_BF16, C(cq), C(ck), 3, 4, 2, d,
+                                      None, 128, 0.0, out, odt, FAKE2, ws, wsb, None)
+    assert bsa(cap=1536) == B.XA_EINVAL                                    # packed V shorter than the keys
+    assert bsa(out=ctypes.c_void_p(0x100008)) == B.XA_EINVAL
+    assert bsa(odt=7) == B.XA_EUNSUPPORTED
+    assert bsa(d=64) == B.XA_EUNSUPPORTED
+    assert bsa(wsb=need_b - 1) == B.XA_EWORKSPACE
