@@ -36,9 +36,9 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.h
 # only for the attention source they were taken on (sha256 of bsa.hip).
 TRAFFIC = {
     "llama8b_32k_8x4k": {
-        "bsa_sha256": "fd3eeb6eccffea54d4e61aa1ece6896fe972db0a732449972c88d687402615fe",
+        "bsa_sha256": "d03933fb44e4c37531c7d2d54a817493a8544cbb9ffc4d975c3cbad80f4d185b",
         "stride": 8, "threshold": 0.95,
-        "hbm_bytes_per_launch": 2.3126e9,   # fetch 2.2485e9 (x1.9999) + write 6.411e7 (x1.0), mean of 8 chunks
+        "hbm_bytes_per_launch": 1.8922e9,   # fetch 1.8282e9 (x1.9999) + write 6.3959e7 (x1.0), mean of 8 chunks
     },
 }
 
@@ -292,7 +292,7 @@ def measure_varlen(a, w, q, k, v):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "lengths": list(w["lengths"]), "tokens": tokens, "q_heads": run.hq,
                    "kv_heads": run.hkv, "head_dim": run.d, "stride": S, "threshold": tau, "block": 128},
-        "roofline": {"bound": "mfma", "kernel": "bsa2_kernel<128, bf16> packed-batch form (block-sparse attention)",
+        "roofline": {"bound": "mfma", "kernel": "bsa3_kernel<128, bf16> packed-batch form (block-sparse attention)",
                      "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(achieved / 2500.0, 4), "traffic": None,
                      "timed_call": "one attention call: record upload, work-order kernels, attention, split merge"},
@@ -472,7 +472,7 @@ def measure(a, w, q, k, v):
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
     if q.dtype == torch.bfloat16 and w["d"] == 128:
-        kernel_name = "bsa2_kernel<128, bf16> (block-sparse attention)"
+        kernel_name = "bsa3_kernel<128, bf16> (block-sparse attention)"
         timed_call = "one attention call: work-order count + sort kernels, then the attention kernel"
     else:
         kernel_name = f"bsa_kernel<{w['d']}, {'fp32 as bf16 hi/lo' if q.dtype == torch.float32 else 'bf16'}>"

@@ -401,7 +401,7 @@ xa_status_t split_qk(const char* fn, const void* q, int64_t& q_tok, int64_t& q_h
   return XA_OK;
 }
 
-// Attention workgroups resident at once on the current device (two per compute unit).
+// Attention workgroups resident at once on the current device.
 int resident_workgroups() {
   static int cached[64];
   int dev = 0;
@@ -409,7 +409,7 @@ int resident_workgroups() {
   if (cached[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = 2 * cus;
+    cached[dev] = bsa_workgroups_per_cu() * cus;
   }
   return cached[dev];
 }

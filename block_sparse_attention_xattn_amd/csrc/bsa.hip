@@ -393,6 +393,12 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// Next work-order entry for this workgroup, longest first (-1: every entry is taken).
+__device__ __forceinline__ int take_entry(const BsaMulti& M) {
+  const int t = atomicAdd(&M.ctl[0], 1);
+  return t < M.ctl[1] ? M.order[t] : -1;
+}
+
 // Segment of work item `item` (kernel-argument segments) and the first item of that segment.
 __device__ __forceinline__ const BsaParams& find_seg(const BsaMulti& M, int item, int& item0) {
   int sidx = 0;
@@ -445,54 +451,36 @@ __device__ __forceinline__ BsaParams varlen_params(const BsaMulti& M, int item, 
   return P;
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong form (bf16, head_dim 128): one workgroup of eight waves per CU.
+// Waves 0-3 (group 0) and 4-7 (group 1) hold the same 128 query rows (32 per
+// wave) and take alternate kept key blocks, each group with
+// its own K and V^T tiles in LDS.  A barrier of all eight waves ends every
+// tick; in each tick one group is in its matrix phase (P V^T of its previous
+// block, then K Q^T of its current block) while the other is in its vector
+// phase (loads of its next tiles are issued, then the online softmax of its
+// current block), so every SIMD holds one wave of each kind.  The two groups'
+// running (max, sum, output) are merged through LDS at the end.
+// ---------------------------------------------------------------------------
 template <int D, typename OutT>
-__device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid);
-
-template <int D, typename OutT, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void bsa2_kernel(BsaMulti M) {
-  __shared__ int s_item;
-  int item = (int)blockIdx.x, part = 0;
-  if (M.order) {
-    // the grid has room for every possible split; only items + splits workgroups take a ticket
-    // (the split count is read only by the workgroups past the item count)
-    const int n_items = M.n_items;
-    if ((int)blockIdx.x >= n_items && (int)blockIdx.x >= n_items + M.ctl[2]) return;
-    if (threadIdx.x == 0) {
-      const int t = atomicAdd(&M.ctl[0], 1);
-      s_item = t < M.ctl[1] ? M.order[t] : -1;
-    }
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(s_item);
-    if (e < 0) return;  // every entry already taken
-    item = e >> 2;
-    part = e & 3;
-  }
-  int item0;
-  if constexpr (VARLEN) {
-    const BsaParams P = varlen_params<D, OutT>(M, item, item0);
-    bsa2_body<D, OutT>(M, P, item, part, item - item0);
-  } else {
-    const BsaParams& P = find_seg(M, item, item0);
-    bsa2_body<D, OutT>(M, P, item, part, item - item0);
-  }
-}
-
-template <int D, typename OutT>
-__device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid) {
-  constexpr int KCH = D / 8;              // 16-byte chunks per K row
+__device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid) {
+  static_assert(D == 128, "ping-pong form: head_dim 128");
+  constexpr int KCH = D / 8;
   constexpr int KTB = 128 * KCH * 16;     // K tile bytes
-  constexpr int VTB = D * 256;            // V^T tile bytes (D rows x 128 keys)
+  constexpr int VTB = D * 256;            // V^T tile bytes
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
-  constexpr int KI = KCH / 2;             // K load instructions per wave
-  constexpr int VI = D / 16;              // V load instructions per wave
-  constexpr float kRescale = 8.0f;        // log2 headroom before the running max moves
-  __shared__ __attribute__((aligned(1024))) char smem[KTB + VTB];
+  constexpr int KI = KCH / 2;
+  constexpr int VI = D / 16;
+  constexpr float kRescale = 8.0f;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (KTB + VTB)];
   __shared__ int s_list[kListMax];
   __shared__ int s_cnt;
-  __shared__ int s_wcnt[4];
+  __shared__ int s_wcnt[8];
 
-  const int wave = wave_id();
+  const int wave8 = wave_id();
+  const int grp = wave8 >> 2;
+  const int wave = wave8 & 3;
   const int lane = lane_id();
   const int n = lane & 31;
   const int hh = lane >> 5;
@@ -514,8 +502,8 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
   f32x16 o[NMD];
 #pragma unroll
   for (int i = 0; i < NMD; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;  // raw (unscaled) reference max of this lane's row
-  float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
+  float m_run = -INFINITY;
+  float l_run = 0.f;
 
   const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
   const int64_t gb0 = P.kv_start / kBlk;
@@ -525,18 +513,15 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
     jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
   }
   int64_t jb_lo = 0;
-  if (part == 1) jb_end = M.mid[item];  // first half of a split item
-  if (part == 2) jb_lo = M.mid[item];   // second half
+  if (part == 1) jb_end = M.mid[item];
+  if (part == 2) jb_lo = M.mid[item];
   const uint8_t* mrow =
       P.mask ? P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
   const bf16* kg = P.k_hi + (int64_t)kvh * P.k_head;
   const bf16* vg = P.vt_hi + (int64_t)kvh * P.vt_head;
-  char* kt = smem;
-  char* vt = smem + KTB;
+  char* kt = smem + grp * (KTB + VTB);
+  char* vt = kt + KTB;
 
-  // Byte offsets of this lane's 16-byte pieces inside a K tile and a V^T tile:
-  // the same for every key block, so a block's loads are one uniform base plus
-  // these (the launcher checks that they fit in 32 bits).
   uint32_t koff[KI], voff[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
@@ -552,9 +537,6 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
     const int ch = (lin & 15) ^ (r & 15);
     voff[i] = (uint32_t)(((int64_t)r * P.vt_pitch + ch * 8) * 2);
   }
-  // Loads of one key block: a buffer descriptor at the block's first row, these
-  // offsets per lane.  Pieces past the descriptor's extent (rows beyond kv_len)
-  // read as zero; those keys are masked before the softmax.
   auto issue_k = [&](int jb) {
     const int64_t j0 = (int64_t)jb * kBlk;
     const int64_t rows = P.kv_len - j0 < kBlk ? P.kv_len - j0 : kBlk;
@@ -568,23 +550,24 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
     for (int i = 0; i < VI; ++i) buf2lds16(rs, voff[i], vt + (wave * VI + i) * 1024);
   };
 
-
+  f32x16 sacc[4];
+  bf16x8 pf[8];
   for (int64_t seg = jb_lo; seg < jb_end; seg += kListMax) {
     const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
     {
-      // each wave scans a quarter of the segment: count, exchange, write
-      const int64_t quarter = ((seg_end - seg + 3) / 4 + 63) / 64 * 64;
-      const int64_t w0 = seg + wave * quarter;
-      const int64_t w1 = w0 + quarter < seg_end ? w0 + quarter : seg_end;
+      // each of the eight waves scans an eighth of the segment: count, exchange, write
+      const int64_t part8 = ((seg_end - seg + 7) / 8 + 63) / 64 * 64;
+      const int64_t w0 = seg + wave8 * part8;
+      const int64_t w1 = w0 + part8 < seg_end ? w0 + part8 : seg_end;
       int mine = 0;
       for (int64_t base = w0; base < w1; base += 64) {
         const int64_t jb = base + lane;
         mine += __popcll(__ballot(jb < w1 && (mrow == nullptr || mrow[jb] != 0)));
       }
-      if (lane == 0) s_wcnt[wave] = mine;
+      if (lane == 0) s_wcnt[wave8] = mine;
       __syncthreads();
       int pos0 = 0;
-      for (int w = 0; w < wave; ++w) pos0 += s_wcnt[w];
+      for (int w = 0; w < wave8; ++w) pos0 += s_wcnt[w];
       for (int64_t base = w0; base < w1; base += 64) {
         const int64_t jb = base + lane;
         const bool keep = jb < w1 && (mrow == nullptr || mrow[jb] != 0);
@@ -592,79 +575,127 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
         if (keep) s_list[pos0 + __popcll(bal & ((1ull << lane) - 1))] = (int)jb;
         pos0 += __popcll(bal);
       }
-      if (wave == 3 && lane == 0) s_cnt = pos0;
+      if (wave8 == 7 && lane == 0) s_cnt = pos0;
     }
     __syncthreads();
     const int cnt = s_cnt;
-    if (cnt > 0) {
-      issue_k(s_list[0]);
-      issue_v(s_list[0]);
-    }
-    for (int it = 0; it < cnt; ++it) {
-      const int jb = __builtin_amdgcn_readfirstlane(s_list[it]);
-      // K(it) landed (V(it) may still be in flight behind it)
-      __builtin_amdgcn_s_waitcnt(0x3f70 | VI);  // vmcnt(VI): only this wave's V loads may remain
-      __syncthreads();
-      f32x16 sacc[4];
+    // this group's blocks: list positions grp, grp + 2, ...; both groups pass the same barriers
+    const int n_own = grp == 0 ? (cnt + 1) / 2 : cnt / 2;
+    const int iters = cnt == 0 ? 0 : (cnt + 1) / 2 + 1;
+    if (n_own > 0) issue_k(s_list[grp]);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    __syncthreads();
+    // matrix phase i: P V^T of block i-1, then K Q^T of block i
+    auto mphase = [&](int i) {
+      if (i >= 1 && i - 1 < n_own) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x16{};
+        for (int k2 = 0; k2 < 8; ++k2)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+          for (int md = 0; md < NMD; ++md)
+            o[md] = mfma32(lds_frag<128>(vt, md * 32 + n, 2 * k2 + hh), pf[k2], o[md]);
+      }
+      if (i < n_own) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            sacc[mt] = mfma32(lds_frag<D>(kt, mt * 32 + n, 2 * kk + hh), qf[kk], sacc[mt]);
+      }
+    };
+    // vector phase i: loads for matrix phase i+1 (K of block i+1, V of block i), softmax of block i
+    auto vphase = [&](int i) {
+      if (i + 1 < n_own) issue_k(s_list[grp + 2 * (i + 1)]);
+      if (i < n_own) {
+        const int jb = __builtin_amdgcn_readfirstlane(s_list[grp + 2 * i]);
+        issue_v(jb);
+        const int64_t key0 = (int64_t)jb * kBlk;
+        if ((key0 + kBlk > P.kv_len) || (P.causal && P.kv_start + key0 + kBlk - 1 > wave_q_lo)) {
+          int64_t lim = P.kv_len - 1 - key0;
+          if (P.causal && q_glob - P.kv_start - key0 < lim) lim = q_glob - P.kv_start - key0;
+          const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int kl = mt * 32 + 8 * (e / 4) + (e % 4);
+              sacc[mt][e] = kl <= lim32 ? sacc[mt][e] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          sacc[mt] = mfma32(lds_frag<D>(kt, mt * 32 + n, 2 * kk + hh), qf[kk], sacc[mt]);
-      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): V(it) landed for this wave
-      __syncthreads();                     // K tile free, V tile complete
-      if (it + 1 < cnt) issue_k(s_list[it + 1]);
-
-      // mask keys past the tail / in the future of this lane's row
-      const int64_t key0 = (int64_t)jb * kBlk;
-      if ((key0 + kBlk > P.kv_len) || (P.causal && P.kv_start + key0 + kBlk - 1 > wave_q_lo)) {
-        int64_t lim = P.kv_len - 1 - key0;
-        if (P.causal && q_glob - P.kv_start - key0 < lim) lim = q_glob - P.kv_start - key0;
-        const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool upd = mx > m_run && (m_run == -INFINITY || (mx - m_run) * c > kRescale);
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+          const float m_new = upd ? mx : m_run;
+          const float alpha = upd ? fast_exp2((m_run - m_new) * c) : 1.f;
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kl = mt * 32 + 8 * (i / 4) + (i % 4);
-            sacc[mt][i] = kl <= lim32 ? sacc[mt][i] : -INFINITY;
+          for (int md = 0; md < NMD; ++md) o[md] *= alpha;
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run * c;
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[k2 >> 1][8 * (k2 & 1) + j], c, -mref));
+            l_run += p;
+            pf[k2][j] = (bf16)p;
           }
       }
-      // online softmax with a lazily moved reference max
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool upd = mx > m_run && (m_run == -INFINITY || (mx - m_run) * c > kRescale);
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        const float m_new = upd ? mx : m_run;
-        const float alpha = upd ? fast_exp2((m_run - m_new) * c) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < NMD; ++md) o[md] *= alpha;
-      }
-      const float mref = m_run == -INFINITY ? 0.f : m_run * c;
-      bf16x8 pf[8];
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[k2 >> 1][8 * (k2 & 1) + j], c, -mref));
-          l_run += p;
-          pf[k2][j] = (bf16)p;
-        }
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2)
-#pragma unroll
-        for (int md = 0; md < NMD; ++md) o[md] = mfma32(lds_frag<128>(vt, md * 32 + n, 2 * k2 + hh), pf[k2], o[md]);
-      __syncthreads();  // V tile free
-      if (it + 1 < cnt) issue_v(s_list[it + 1]);
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads for the next matrix phase landed
+    };
+    // Both groups run the same loop; group 1 starts one barrier later and group 0 passes one more barrier
+    // at the end (the hardware barrier counts waves, and these branches are uniform per wave), so group
+    // 1's matrix phase i meets group 0's vector phase i and the other way round.
+    if (grp == 1) __syncthreads();
+    for (int i = 0; i < iters; ++i) {
+      mphase(i);
+      __syncthreads();
+      vphase(i);
+      __syncthreads();
     }
-    __syncthreads();  // s_list is rewritten by the next segment
+    if (grp == 0) __syncthreads();
+  }
+
+  // merge group 1's running state into group 0's (same lane layout), through LDS
+  __syncthreads();
+  f32x4* xo = reinterpret_cast<f32x4*>(smem);                              // [4 waves][16][64 lanes]
+  float* xm = reinterpret_cast<float*>(smem + 4 * 16 * 64 * sizeof(f32x4));  // [4 waves][64 lanes]
+  float* xl = xm + 4 * 64;
+  if (grp == 1) {
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        xo[(wave * 16 + md * 4 + g4) * 64 + lane] =
+            f32x4{o[md][g4 * 4], o[md][g4 * 4 + 1], o[md][g4 * 4 + 2], o[md][g4 * 4 + 3]};
+    xm[wave * 64 + lane] = m_run;
+    xl[wave * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = xm[wave * 64 + lane];
+    const float l1 = xl[wave * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m) * c);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - m) * c);
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 y = xo[(wave * 16 + md * 4 + g4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[md][g4 * 4 + e] = o[md][g4 * 4 + e] * a0 + y[e] * a1;
+      }
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32);
@@ -674,7 +705,6 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
     lse_v = (m_run * c + log2f(l_row)) * kLn2;
   }
   if (part != 0) {
-    // half of a split item: fp32 partial result, merged by split_merge_kernel
     const size_t ps = (size_t)(2 * M.slot[item] + part - 1) * kBlk + wave * 32 + n;
     float* po = M.part_o + ps * D;
 #pragma unroll
@@ -708,6 +738,30 @@ __device__ __forceinline__ void bsa2_body(const BsaMulti& M, const BsaParams& P,
       }
     }
   if (hh == 0) P.lse[(int64_t)h * P.q_len + row] = lse_v;
+}
+
+template <int D, typename OutT, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void bsa3_kernel(BsaMulti M) {
+  __shared__ int s_item;
+  int item = (int)blockIdx.x, part = 0;
+  if (M.order) {
+    const int n_items = M.n_items;
+    if ((int)blockIdx.x >= n_items && (int)blockIdx.x >= n_items + M.ctl[2]) return;
+    if (threadIdx.x == 0) s_item = take_entry(M);
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(s_item);
+    if (e < 0) return;
+    item = e >> 2;
+    part = e & 3;
+  }
+  int item0;
+  if constexpr (VARLEN) {
+    const BsaParams P = varlen_params<D, OutT>(M, item, item0);
+    bsa3_body<D, OutT>(M, P, item, part, item - item0);
+  } else {
+    const BsaParams& P = find_seg(M, item, item0);
+    bsa3_body<D, OutT>(M, P, item, part, item - item0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1038,6 +1092,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(BsaMulti M) {
   for (int k = (int)blockIdx.x; k < M.ctl[2]; k += (int)gridDim.x) split_merge_one<D, OutT, VARLEN>(M, k);
 }
 
+// One attention workgroup (eight waves, 132 KiB of LDS) per compute unit.
+int bsa_workgroups_per_cu() { return 1; }
+
 // Host tables reach device memory through the arguments of a small kernel, in stream order.
 constexpr int kBlobWords = 384;
 struct Blob {
@@ -1060,7 +1117,7 @@ hipError_t upload_words(const void* src, size_t bytes, void* dst, hipStream_t s)
 }
 
 // Explicit instantiation helpers used by the ABI layer.
-// bsa2_kernel addresses a lane's pieces of a K / V^T tile with 32-bit byte offsets.
+// bsa3_kernel addresses a lane's pieces of a K / V^T tile with 32-bit byte offsets.
 static bool tile_offsets_fit(const BsaParams* segs, int n_seg, int D) {
   for (int i = 0; i < n_seg; ++i)
     if ((127 * segs[i].k_tok + D) * 2 >= ((int64_t)1 << 32) ||
@@ -1098,7 +1155,7 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
           m.part_lse = plan->part_lse;
           grid = total + plan->max_split;  // entries: items plus halves of split items
         }
-        hipLaunchKernelGGL((bsa2_kernel<D, OutT, false>), dim3(grid), dim3(256), 0, s, m);
+        hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
         if (plan && plan->max_split > 0)
           hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(plan->max_split, 64)), dim3(256), 0, s,
                              m);
@@ -1132,7 +1189,7 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   m.split_items = plan->split_items;
   m.part_o = plan->part_o;
   m.part_lse = plan->part_lse;
-  hipLaunchKernelGGL((bsa2_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(256), 0, s, m);
+  hipLaunchKernelGGL((bsa3_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(512), 0, s, m);
   if (plan->max_split > 0)
     hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
   return hipGetLastError();

@@ -251,7 +251,7 @@ def test_segments_work_order():
 
     Exact integer checks: every item's kept-tile count equals the mask row's
     count up to the causal limit (as a multiset over items); the split items
-    are the ones of at least 32 tiles longer than total / (2 x compute units)
+    are the ones of at least 32 tiles longer than total / compute units
     (none here: rows of at most 10 blocks), each with a median inside its row;
     the entries are the unsplit items once (part 0) and the split items twice
     (parts 1 and 2), sorted by descending count, and every entry was taken (the
@@ -297,7 +297,7 @@ def test_segments_work_order():
     expect += [int(mask[h, qb, 6:6 + min(qb + 1, 4)].sum()) for h in range(hq) for qb in range(nqb)]
     expect += [int(row.sum())] * (hq * nqb)
     assert sorted(weights.tolist()) == sorted(expect)
-    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    slots = torch.cuda.get_device_properties(0).multi_processor_count  # one attention workgroup per CU
     thr = int(weights.sum()) // slots
     split = {i for i in range(n) if weights[i] >= 32 and weights[i] > thr}
     assert ctl[1] == n + n_split and n_split == len(split) and ctl[0] >= ctl[1]
