@@ -349,3 +349,36 @@ def test_segments_split_items():
             O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True)]
     for (go, gl), (ro, rl) in zip(outs, refs):
         PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
+
+
+def test_rows_longer_than_one_block_list():
+    """Rows of more than 1024 candidate key blocks are listed 1024 blocks at a time: dense attention over
+    1100 blocks (no work order), and a segmented call over 2200 blocks at mask density 0.9 whose rows are
+    split in two (each half again longer than 1024 blocks); out and LSE match the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d = 4, 2, 128
+    for n_kb, dense in ((1100, True), (2200, False)):
+        kv = n_kb * 128
+        q = _rand((128, hq, d), torch.bfloat16, 90 + n_kb)
+        k = _rand((kv, hkv, d), torch.bfloat16, 91 + n_kb)
+        v = _rand((kv, hkv, d), torch.bfloat16, 92 + n_kb)
+        qd, kd = q.to(DEV), k.to(DEV)
+        packed = B.PackedV(kv, hkv, d, torch.bfloat16, DEV)
+        B.bsa_pack_v(v.to(DEV), packed, 0)
+        if dense:
+            out, lse = B.bsa_prefill_packed(qd, kd, packed, 0, kv, 0, None, 0, False)
+            mask = None
+        else:
+            rng = np.random.default_rng(12)
+            mask = (rng.random((hq, 1, n_kb)) < 0.9).astype(np.uint8)
+            out = torch.empty(128, hq, d, dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty(hq, 128, dtype=torch.float32, device=DEV)
+            segs = [dict(k=kd, kv_start=0, v_token_offset=0, block_mask=torch.from_numpy(mask).to(DEV), causal=False,
+                         out=out, lse=lse)]
+            ws = B.workspace(B.bsa_prefill_segments_workspace_size(128, hq, d, 1), DEV)
+            B.bsa_prefill_segments(qd, packed, kv, segs, ws=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:12].cpu().numpy().view(np.int32)[2]) == hq, "expected every row split"
+        torch.cuda.synchronize()
+        ro, rl = O.bsa(_np(q), _np(k), _np(v), kv, 0, mask, 0, False)
+        PAR.check_out_lse(_np(out), _np(lse), ro, rl, PAR.OUT_ATOL_BF16)
