@@ -37,8 +37,8 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.h
 TRAFFIC = {
     "llama8b_32k_8x4k": {
         "bsa_sha256": "d03933fb44e4c37531c7d2d54a817493a8544cbb9ffc4d975c3cbad80f4d185b",
-        "stride": 8, "threshold": 0.95,
-        "hbm_bytes_per_launch": 1.8922e9,   # fetch 1.8282e9 (x1.9999) + write 6.3959e7 (x1.0), mean of 8 chunks
+        "stride": 8, "threshold": 0.95, "fused": True,
+        "hbm_bytes_per_launch": 1.9289e9,   # fetch 1.8948e9 (x1.9999) + write 3.4112e7 (x1.0), mean of 8 chunks
     },
 }
 
@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--offload", action="store_true",
                     help="history K/V in pinned host cache blocks, kept blocks copied back through a device ring")
     ap.add_argument("--group", type=int, default=8, help="cache blocks per ring group (offload)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="history and in-chunk attention as two segments merged by LSE (the pages' composition)")
     return ap.parse_args()
 
 
@@ -377,7 +379,8 @@ def measure(a, w, q, k, v):
     if "q_start_pos" in w:
         starts = [w["q_start_pos"]]
     run = ChunkedPrefill(q, k, v, chunk=w["chunk"], stride=w["stride"], threshold=w["threshold"],
-                         chunk_starts=starts, cache_block=w.get("cache_block"), estimator=a.estimator)
+                         chunk_starts=starts, cache_block=w.get("cache_block"), estimator=a.estimator,
+                         fused=not a.unfused)
     run.pack_history()
     torch.cuda.synchronize()
     for _ in range(a.warmup):
@@ -415,7 +418,8 @@ def measure(a, w, q, k, v):
         return inner
 
     run.estimate = timed("estimate", orig_est)
-    run.merge = timed("merge", orig_merge)
+    if not run.fused:
+        run.merge = timed("merge", orig_merge)
     run.pack = timed("pack", orig_pack)
     run.reduce = timed("reduce", orig_reduce)
     B.bsa_prefill_packed = wrap(orig_bsa)
@@ -458,6 +462,22 @@ def measure(a, w, q, k, v):
         c_len = w["chunk"]
         per_merge = 3 * c_len * w["hq"] * w["d"] * q.element_size() + 3 * w["hq"] * c_len * 4
         hbm["merge_gbs"] = round(per_merge * n_merge / (parts["merge"] * 1e-3) / 1e9, 1)
+    if n_merge and not parts.get("merge"):
+        # the fused step has no merge: the LSE merge is timed alone on two partials of the chunk's shape
+        c_len = w["chunk"]
+        oa, ob = (torch.randn(c_len, w["hq"], w["d"], device=q.device).to(q.dtype) for _ in range(2))
+        la, lb = (torch.randn(w["hq"], c_len, device=q.device) for _ in range(2))
+        oo, lo = torch.empty_like(oa), torch.empty_like(la)
+        for _ in range(3):
+            B.attn_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(20):
+            B.attn_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        per_merge = 3 * c_len * w["hq"] * w["d"] * q.element_size() + 3 * w["hq"] * c_len * 4
+        hbm["merge_gbs_standalone"] = round(per_merge * 20 / (m0.elapsed_time(m1) * 1e-3) / 1e9, 1)
     red = [b for b in run.bufs if b.keep_any is not None]
     if red and parts.get("reduce"):
         per_red = sum(b.mask.shape[0] * b.mask.shape[1] * b.keep_any.shape[0] * (w["cache_block"] // 128)
@@ -479,8 +499,8 @@ def measure(a, w, q, k, v):
         timed_call = "one attention call per segment: one kernel"
     rec = TRAFFIC.get(a.workload)
     traffic = None
-    if rec and rec["bsa_sha256"] == source_sha(ATTN_SRC) and (rec["stride"], rec["threshold"]) == (
-            w["stride"], w["threshold"]):
+    if rec and rec["bsa_sha256"] == source_sha(ATTN_SRC) and (rec["stride"], rec["threshold"], rec["fused"]) == (
+            w["stride"], w["threshold"], run.fused):
         traffic = rec["hbm_bytes_per_launch"]
 
     out = {
@@ -498,7 +518,8 @@ def measure(a, w, q, k, v):
         "data": "synthetic",
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
                    "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
-                   "block": 128, "chunks_timed": len(run.starts), "estimator": a.estimator},
+                   "block": 128, "chunks_timed": len(run.starts), "estimator": a.estimator,
+                   "attention": "one causal pass per chunk" if run.fused else "history + chunk segments, LSE merge"},
         "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,

@@ -18,8 +18,13 @@ then not read by the estimate.
 V is kept packed once per layer in the attention kernel's layout: each chunk
 packs its own V rows when it starts (bsa_pack_v), and both attention calls
 read the packed buffer (one bsa_prefill_segments launch for bf16, head_dim
-128; two bsa_prefill_packed calls otherwise).  All buffers are allocated up
-front; a step only enqueues library calls on the current stream.
+128; two bsa_prefill_packed calls otherwise).  With a block mask per chunk
+(bf16, head_dim 128, fused=True) steps 2-4 are one causal pass over keys
+[0 : p+C) with the chunk's mask row: the history lies before every query,
+so the causal rule only acts on the chunk's own keys and the result is the
+merged one (up to rounding) without writing the two partial results.  All
+buffers are allocated up front; a step only enqueues library calls on the
+current stream.
 """
 from __future__ import annotations
 
@@ -54,7 +59,8 @@ class ChunkedPrefill:
     """
 
     def __init__(self, q, k, v, chunk: int, stride: int, threshold: float, block: int = 128,
-                 chunk_starts=None, cache_block: int | None = None, out_dtype=None, estimator: str = "full"):
+                 chunk_starts=None, cache_block: int | None = None, out_dtype=None, estimator: str = "full",
+                 fused: bool = True):
         self.q, self.k, self.v = q, k, v
         self.L, self.hq, self.d = q.shape
         self.hkv = k.shape[1]
@@ -65,6 +71,9 @@ class ChunkedPrefill:
         if estimator == "downsampled" and not cache_block:
             raise ValueError("the downsampled estimator selects cache blocks: pass cache_block")
         self.estimator = estimator
+        # fused: with a block mask per chunk (not the cache-block form), a chunk's history and own keys as one
+        # causal pass over keys [0, p + C) (bf16, head_dim 128)
+        self.fused = fused and q.dtype == torch.bfloat16 and self.d == 128 and not cache_block
         dev = q.device
         self.out_dtype = q.dtype if out_dtype is None else out_dtype
         self.starts = list(range(0, self.L, chunk)) if chunk_starts is None else list(chunk_starts)
@@ -152,10 +161,17 @@ class ChunkedPrefill:
                                      keep_any_blocks=b.keep_any_blocks)
 
     def attend(self, b: ChunkBuffers):
-        """History (no causal rule) and the chunk's own keys (causal) in one segmented launch."""
+        """History (no causal rule) and the chunk's own keys (causal) in one segmented launch, or, fused,
+        one causal pass over both with the chunk's mask row (the history lies before every query, so the causal
+        rule only acts on the chunk's own keys), written straight to the output with no merge."""
         p = b.p
         c = self._len(b)
         qc = self.q[p:p + c]
+        if self.fused:
+            seg = dict(k=self.k[:p + c], kv_start=0, v_token_offset=0, block_mask=b.mask, causal=True,
+                       out=self.out[p:p + c], lse=b.lse)
+            B.bsa_prefill_segments(qc, self.packed, p, [seg], ws=self.seg_ws)
+            return
         segs = []
         if p > 0:
             if b.keep_any_blocks is not None:
@@ -164,7 +180,8 @@ class ChunkedPrefill:
             else:
                 segs.append(dict(k=self.k[:p], kv_start=0, v_token_offset=0, block_mask=b.mask, causal=False,
                                  out=b.o_hist, lse=b.l_hist))
-        cur_mask = None if b.keep_any_blocks is not None else b.mask
+        # the cache-block form and the downsampled estimator attend the chunk's own keys densely
+        cur_mask = None if (b.keep_any_blocks is not None or self.estimator == "downsampled") else b.mask
         segs.append(dict(k=self.k[p:p + c], kv_start=p, v_token_offset=p, block_mask=cur_mask, causal=True,
                          out=b.o_cur, lse=b.l_cur if p > 0 else b.lse))
         if self.q.dtype == torch.bfloat16 and self.d == 128:
@@ -177,7 +194,7 @@ class ChunkedPrefill:
                                      mask_row_stride=g.get("mask_row_stride"))
 
     def merge(self, b: ChunkBuffers):
-        if b.p == 0:
+        if b.p == 0 or self.fused:
             return
         c = self._len(b)
         B.attn_merge(b.o_hist, b.l_hist, b.o_cur, b.l_cur, o_out=self.out[b.p:b.p + c], lse_out=b.lse)

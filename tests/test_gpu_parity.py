@@ -170,12 +170,16 @@ def test_tiny_chunked_prefill_end_to_end():
     PAR.check_out_lse(_np(out), _np(b.lse), ref["out"], ref["lse"], PAR.OUT_ATOL_F32)
 
 
-def test_small_multichunk_prefill_end_to_end():
+@pytest.mark.parametrize("fused", [True, False])
+def test_small_multichunk_prefill_end_to_end(fused):
+    """Four chunks against the oracle's chunked prefill (history + chunk attention, LSE merge), with the GPU
+    running each chunk as one causal pass (fused) or as the two segments and the merge."""
     from block_sparse_attention_xattn_amd import synthetic
     from block_sparse_attention_xattn_amd.prefill import ChunkedPrefill
     q, k, v = synthetic.long_context(4096, 8, 2, 128, n_needles=4, seed=7)
     ref = O.chunked_prefill(_np(q), _np(k), _np(v), 1024, 8, 0.9)
-    run = ChunkedPrefill(q.to(DEV), k.to(DEV), v.to(DEV), chunk=1024, stride=8, threshold=0.9)
+    run = ChunkedPrefill(q.to(DEV), k.to(DEV), v.to(DEV), chunk=1024, stride=8, threshold=0.9, fused=fused)
+    assert run.fused == fused
     out = run.run()
     torch.cuda.synchronize()
     same = True
