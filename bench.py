@@ -36,12 +36,12 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_xattn_amd", "csrc", "bsa.h
 # only for the attention source they were taken on (sha256 of bsa.hip).
 TRAFFIC = {
     "llama8b_32k_8x4k": [
-        {"bsa_sha256": "d03933fb44e4c37531c7d2d54a817493a8544cbb9ffc4d975c3cbad80f4d185b",
+        {"bsa_sha256": "6c90de2fb472d9f06615aa0fc362aac9e8785bbbd95a1904242879aa93793da0",
          "stride": 8, "threshold": 0.95, "fused": False,
-         "hbm_bytes_per_launch": 1.8922e9},   # fetch 1.8282e9 (x1.9999) + write 6.3959e7 (x1.0), mean of 8 chunks
-        {"bsa_sha256": "d03933fb44e4c37531c7d2d54a817493a8544cbb9ffc4d975c3cbad80f4d185b",
+         "hbm_bytes_per_launch": 1.9062e9},   # fetch 1.8423e9 (x1.9999) + write 6.3959e7 (x1.0), mean of 8 chunks
+        {"bsa_sha256": "6c90de2fb472d9f06615aa0fc362aac9e8785bbbd95a1904242879aa93793da0",
          "stride": 8, "threshold": 0.95, "fused": True,
-         "hbm_bytes_per_launch": 1.9289e9},   # fetch 1.8948e9 (x1.9999) + write 3.4112e7 (x1.0), mean of 8 chunks
+         "hbm_bytes_per_launch": 1.9317e9},   # fetch 1.8976e9 (x1.9999) + write 3.4112e7 (x1.0), mean of 8 chunks
     ],
 }
 
@@ -65,9 +65,8 @@ def parse():
                     help="history K/V in pinned host cache blocks, kept blocks copied back through a device ring")
     ap.add_argument("--group", type=int, default=8, help="cache blocks per ring group (offload)")
     ap.add_argument("--fused", action="store_true",
-                    help="time each chunk's history + chunk attention as one causal pass (no merge) as the headline; "
-                         "by default the headline is the pages' composition (two segments, LSE merge) and the fused "
-                         "pass is reported beside it")
+                    help="time each chunk's history + chunk attention as one causal pass (no partials, no merge); "
+                         "by default a step is the pages' composition (two segments, LSE merge)")
     return ap.parse_args()
 
 
@@ -370,16 +369,7 @@ def main():
     w = dict(base)
     w["stride"] = a.stride if a.stride is not None else w.get("stride", 8)
     w["threshold"] = a.threshold if a.threshold is not None else w.get("threshold", 0.9)
-    if a.offload:
-        out = measure_offload(a, w, q, k, v)
-    else:
-        out = measure(a, w, q, k, v)
-        if not a.fused and out["config"].get("fused_eligible"):
-            # the same step with each chunk's attention as one causal pass (no partials, no merge)
-            f = measure(a, w, q, k, v, fused=True)
-            out["fused_pass"] = {"ms_per_step": f["ms_per_step"], "tokens_per_s": f["value"],
-                                 "attention_tflops": f["roofline"]["achieved"], "frac": f["roofline"]["frac"],
-                                 "traffic": f["roofline"]["traffic"]}
+    out = measure_offload(a, w, q, k, v) if a.offload else measure(a, w, q, k, v)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_groups, w)
     print(json.dumps(out))
@@ -535,8 +525,7 @@ def measure(a, w, q, k, v, fused=None):
         "config": {"workload": a.workload, "tokens": w["L"], "chunk": w["chunk"], "q_heads": w["hq"],
                    "kv_heads": w["hkv"], "head_dim": w["d"], "stride": w["stride"], "threshold": w["threshold"],
                    "block": 128, "chunks_timed": len(run.starts), "estimator": a.estimator,
-                   "attention": "one causal pass per chunk" if run.fused else "history + chunk segments, LSE merge",
-                   "fused_eligible": bool(q.dtype == torch.bfloat16 and w["d"] == 128 and not w.get("cache_block"))},
+                   "attention": "one causal pass per chunk" if run.fused else "history + chunk segments, LSE merge"},
         "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(bsa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bsa_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,

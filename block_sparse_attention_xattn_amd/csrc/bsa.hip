@@ -354,22 +354,15 @@ __global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel.
+// Tile layout of the bf16 kernel (bsa3_kernel below).
 //
-//   * workgroup = (query head, 128-row query block), 4 waves; wave w owns
-//     query rows 32w .. 32w+31 against all 128 keys of each kept block, so no
-//     cross-wave merge is needed;
-//   * two workgroups share a CU (<= 256 registers per wave, 68 KiB LDS each):
-//     their barriers are independent, so one workgroup's softmax (VALU) runs
-//     while the other's QK^T / PV (MFMA) run on the same SIMDs;
-//   * K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no
+//   * wave w of a group owns query rows 32w .. 32w+31 against all 128 keys of
+//     each kept block, so no cross-wave merge is needed inside a group;
+//   * K and V^T tiles go global -> LDS with buffer_load_dwordx4 ... lds (no
 //     staging registers): lane L of a wave-instruction lands at byte 16*L of a
 //     1 KiB run, so the 16-byte chunk a lane fetches is chosen such that LDS
 //     slot s of row r holds chunk s ^ (r mod 16) (XOR swizzle: fragment reads
 //     of 16 consecutive rows hit 16 distinct bank groups);
-//   * one K and one V buffer: the next K tile is fetched as soon as every
-//     wave has finished Q K^T, the next V tile as soon as P V is done, so each
-//     fetch overlaps the other half of the block's work;
 //   * the running max is only moved when a row's max grows by more than 2^8
 //     (P <= 256 in between), so the O rescale is rare.
 // ---------------------------------------------------------------------------
@@ -377,10 +370,6 @@ template <int D>
 __device__ __forceinline__ bf16x8 lds_frag(const char* tile, int row, int chunk) {
   constexpr int KCH = D / 8;
   return *reinterpret_cast<const bf16x8*>(tile + row * (KCH * 16) + ((chunk ^ (row & (KCH - 1))) << 4));
-}
-
-__device__ __forceinline__ void g2lds16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 // Raw buffer descriptor over [base, base + bytes); loads past the end return zero.
@@ -405,12 +394,6 @@ __device__ __forceinline__ const BsaParams& find_seg(const BsaMulti& M, int item
   while (sidx + 1 < M.n_seg && item >= M.wg_end[sidx]) ++sidx;
   item0 = sidx ? M.wg_end[sidx - 1] : 0;
   return M.seg[sidx];
-}
-
-__device__ __forceinline__ int64_t rfl64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Packed batch: the sequence of work item `item` (binary search of the records' item prefix ends,

@@ -49,6 +49,13 @@ __host__ __device__ __forceinline__ int kSigma(int s) {
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A wave-uniform 64-bit value in scalar registers.
+__device__ __forceinline__ int64_t rfl64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Spread consecutive work items over the 8 XCDs in contiguous runs: the

@@ -191,12 +191,6 @@ __device__ __forceinline__ const VarlenSeq& varlen_seq(const VarlenSeq* seqs, in
   return v;
 }
 
-__device__ __forceinline__ int64_t rfl64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 template <int HALF>
 __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
   constexpr int TILE = 256;

@@ -136,6 +136,7 @@ EST_CASES = [
     (2, 1, 64, torch.bfloat16, 256, 256, 2, 0.9, 4),
     (7, 1, 128, torch.bfloat16, 256, 1792, 8, 1.0, 5),
     (4, 2, 64, torch.float32, 640, 1280, 8, 0.5, 6),
+    (4, 2, 128, torch.bfloat16, 128, 3968, 8, 0.0, 7),   # threshold 0: only block 0 and the diagonal, one query block
 ]
 
 
