@@ -505,32 +505,31 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
   char* kt = smem + grp * (KTB + VTB);
   char* vt = kt + KTB;
 
-  uint32_t koff[KI], voff[VI];
+  // Piece i of this wave's share of a K (V^T) tile covers rows r = 32 wave + 4 i + lane / 16 (16 lanes of
+  // 16 bytes per 256-byte row), lane chunk (lane % 16) ^ (r % 16).  r % 16 = 4 (i % 4) + lane / 16, so the
+  // byte offset is kx[i % 4] + i * 4 rows: four per-lane bases per tile instead of eight offsets.
+  static_assert(KCH == 16 && KI == 8 && VI == 8, "tile pieces: 16 chunks per row, 8 pieces per wave");
+  uint32_t kx[4], vx[4];
 #pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int lin = (wave * KI + i) * 64 + lane;
-    const int r = lin / KCH;
-    const int ch = (lin % KCH) ^ (r & (KCH - 1));
-    koff[i] = (uint32_t)(((int64_t)r * P.k_tok + ch * 8) * 2);
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + (lane >> 4);
+    const int ch = (lane & 15) ^ (4 * j + (lane >> 4));
+    kx[j] = (uint32_t)(((int64_t)r * P.k_tok + ch * 8) * 2);
+    vx[j] = (uint32_t)(((int64_t)r * P.vt_pitch + ch * 8) * 2);
   }
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int lin = (wave * VI + i) * 64 + lane;
-    const int r = lin >> 4;
-    const int ch = (lin & 15) ^ (r & 15);
-    voff[i] = (uint32_t)(((int64_t)r * P.vt_pitch + ch * 8) * 2);
-  }
+  const uint32_t kstep = (uint32_t)(8 * P.k_tok);     // 4 rows of K, bytes
+  const uint32_t vstep = (uint32_t)(8 * P.vt_pitch);  // 4 rows of V^T, bytes
   auto issue_k = [&](int jb) {
     const int64_t j0 = (int64_t)jb * kBlk;
     const int64_t rows = P.kv_len - j0 < kBlk ? P.kv_len - j0 : kBlk;
     const auto rs = tile_rsrc(kg + j0 * P.k_tok, (uint32_t)(((rows - 1) * P.k_tok + D) * 2));
 #pragma unroll
-    for (int i = 0; i < KI; ++i) buf2lds16(rs, koff[i], kt + (wave * KI + i) * 1024);
+    for (int i = 0; i < KI; ++i) buf2lds16(rs, kx[i & 3] + i * kstep, kt + (wave * KI + i) * 1024);
   };
   auto issue_v = [&](int jb) {
     const auto rs = tile_rsrc(vg + (int64_t)jb * kBlk, (uint32_t)(((int64_t)(D - 1) * P.vt_pitch + kBlk) * 2));
 #pragma unroll
-    for (int i = 0; i < VI; ++i) buf2lds16(rs, voff[i], vt + (wave * VI + i) * 1024);
+    for (int i = 0; i < VI; ++i) buf2lds16(rs, vx[i & 3] + i * vstep, vt + (wave * VI + i) * 1024);
   };
 
   f32x16 sacc[4];
@@ -568,23 +567,36 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     if (n_own > 0) issue_k(s_list[grp]);
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
-    // matrix phase i: P V^T of block i-1, then K Q^T of block i
+    // matrix phase i: P V^T of block i-1, then K Q^T of block i.  Operand fragments are read one
+    // contraction step ahead (a ring of four), so an LDS read has four MFMAs to land.
+    static_assert(NMD == 4, "fragment ring: four output / score tiles");
     auto mphase = [&](int i) {
+      bf16x8 fr[4];
       if (i >= 1 && i - 1 < n_own) {
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) fr[md] = lds_frag<128>(vt, md * 32 + n, hh);
 #pragma unroll
         for (int k2 = 0; k2 < 8; ++k2)
 #pragma unroll
-          for (int md = 0; md < NMD; ++md)
-            o[md] = mfma32(lds_frag<128>(vt, md * 32 + n, 2 * k2 + hh), pf[k2], o[md]);
+          for (int md = 0; md < NMD; ++md) {
+            o[md] = mfma32(fr[md], pf[k2], o[md]);
+            if (k2 + 1 < 8) fr[md] = lds_frag<128>(vt, md * 32 + n, 2 * (k2 + 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of the next MFMAs
+          }
       }
       if (i < n_own) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fr[mt] = lds_frag<D>(kt, mt * 32 + n, hh);
+#pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            sacc[mt] = mfma32(lds_frag<D>(kt, mt * 32 + n, 2 * kk + hh), qf[kk], sacc[mt]);
+          for (int mt = 0; mt < 4; ++mt) {
+            sacc[mt] = mfma32(fr[mt], qf[kk], sacc[mt]);
+            if (kk + 1 < NKK) fr[mt] = lds_frag<D>(kt, mt * 32 + n, 2 * (kk + 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of the next MFMAs
+          }
       }
     };
     // vector phase i: loads for matrix phase i+1 (K of block i+1, V of block i), softmax of block i
