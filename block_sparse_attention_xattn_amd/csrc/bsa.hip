@@ -471,14 +471,14 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
   int h, qb;
   bsa_decode(bid, P.group, P.hkv, P.n_qb, h, qb);
   const int kvh = h / P.group;
-  const int64_t row = (int64_t)qb * kBlk + wave * 32 + n;
-  const int64_t q_glob = P.q_start + row;
-  const int64_t wave_q_lo = P.q_start + (int64_t)qb * kBlk + wave * 32;
+  // this lane's query row is row0 + n (row0 wave-uniform); no 64-bit per-lane index stays live
+  const int64_t row0 = (int64_t)qb * kBlk + wave * 32;
+  const int64_t wave_q_lo = P.q_start + row0;
   const float c = P.scale_log2;
 
   bf16x8 qf[NKK];
   {
-    const int64_t off = row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+    const int64_t off = (row0 + n) * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q_hi + off + kk * 16));
   }
@@ -608,7 +608,8 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
         const int64_t key0 = (int64_t)jb * kBlk;
         if ((key0 + kBlk > P.kv_len) || (P.causal && P.kv_start + key0 + kBlk - 1 > wave_q_lo)) {
           int64_t lim = P.kv_len - 1 - key0;
-          if (P.causal && q_glob - P.kv_start - key0 < lim) lim = q_glob - P.kv_start - key0;
+          const int64_t qlim = wave_q_lo - P.kv_start - key0 + n;  // causal limit of this lane's row
+          if (P.causal && qlim < lim) lim = qlim;
           const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
@@ -714,7 +715,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     return;
   }
   OutT* out = reinterpret_cast<OutT*>(P.out);
-  const int64_t obase = row * ((int64_t)P.hq * D) + (int64_t)h * D;
+  const int64_t obase = (row0 + n) * ((int64_t)P.hq * D) + (int64_t)h * D;
 #pragma unroll
   for (int md = 0; md < NMD; ++md)
 #pragma unroll
@@ -732,7 +733,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
         *reinterpret_cast<f32x4*>(out + obase + d0) = f32x4{v[0], v[1], v[2], v[3]};
       }
     }
-  if (hh == 0) P.lse[(int64_t)h * P.q_len + row] = lse_v;
+  if (hh == 0) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
 }
 
 template <int D, typename OutT, bool VARLEN>
