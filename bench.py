@@ -17,6 +17,7 @@ oracle timed on one key/value-head group of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -241,10 +242,12 @@ def measure_varlen(a, w, q, k, v):
         run.run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    # every event is created before the timed region (creating one can stall the host)
+    ev_pool = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
     ev = []
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for st in range(a.steps):
+        e = ev_pool[st]
         e[0].record(stream)
         run.pack()
         e[1].record(stream)
@@ -346,6 +349,8 @@ def main():
     if a.copy_mib:
         copy_probe(a.copy_mib)
         return
+    # no garbage-collector pauses inside the timed regions; collected explicitly between measurements
+    gc.disable()
     from block_sparse_attention_xattn_amd import synthetic
 
     base = dict(synthetic.WORKLOADS[a.workload])
@@ -364,6 +369,7 @@ def main():
         for stride in base.get("strides", (base.get("stride", 8),)):
             for tau in base.get("thresholds", (base.get("threshold", 0.9),)):
                 w = dict(base, stride=stride, threshold=tau)
+                gc.collect()
                 print(json.dumps(measure(a, w, q, k, v)), flush=True)
         return
     w = dict(base)
@@ -393,12 +399,14 @@ def measure(a, w, q, k, v, fused=None):
         run.run()
     torch.cuda.synchronize()
 
-    # timed region, with events around every library call
+    # timed region, with events around every library call; the events are created beforehand (creating one
+    # inside the timed region can stall the host for tens of milliseconds)
     stream = torch.cuda.current_stream()
     ev = []
+    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(12 * len(run.bufs) * a.steps + 8)]
 
     def mark(tag):
-        e = torch.cuda.Event(enable_timing=True)
+        e = ev_pool.pop() if ev_pool else torch.cuda.Event(enable_timing=True)
         e.record(stream)
         ev.append((tag, e))
 
