@@ -675,7 +675,15 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     xl[wave * 64 + lane] = l_run;
   }
   __syncthreads();
-  if (grp == 1) return;
+  // bf16 rows of a whole item go out through LDS: the eight waves then write whole 256-byte rows (a lane's
+  // own row pieces are 8 bytes in rows 8 KiB apart, which the memory system takes as partial-line writes)
+  constexpr bool kStageOut = sizeof(OutT) == 2;
+  const bool stage = kStageOut && part == 0;
+  constexpr int kStgPitch = D * 2 + 16;  // padded row pitch: the 8-byte writes of a column spread over banks
+  char* stg = smem + 80 * 1024;          // after group 1's state (64 KiB + 2 KiB)
+  static_assert(80 * 1024 + 128 * kStgPitch <= 2 * (KTB + VTB), "staging fits the tile buffers");
+  if (grp == 1 && !stage) return;
+  if (grp == 0) {
   {
     const float m1 = xm[wave * 64 + lane];
     const float l1 = xl[wave * 64 + lane];
@@ -714,6 +722,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     if (hh == 0) M.part_lse[ps] = lse_v;
     return;
   }
+  if (hh == 0) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
   OutT* out = reinterpret_cast<OutT*>(P.out);
   const int64_t obase = (row0 + n) * ((int64_t)P.hq * D) + (int64_t)h * D;
 #pragma unroll
@@ -724,16 +733,30 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = o[md][g4 * 4 + e] * inv;
-      if constexpr (sizeof(OutT) == 2) {
+      if constexpr (kStageOut) {
         bf16x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[e] = (bf16)v[e];
-        *reinterpret_cast<u32x2*>(out + obase + d0) = __builtin_bit_cast(u32x2, pk);
+        *reinterpret_cast<u32x2*>(stg + (wave * 32 + n) * kStgPitch + d0 * 2) = __builtin_bit_cast(u32x2, pk);
       } else {
         *reinterpret_cast<f32x4*>(out + obase + d0) = f32x4{v[0], v[1], v[2], v[3]};
       }
     }
-  if (hh == 0) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
+  if (!stage) return;
+  }
+  __syncthreads();
+  // 128 rows x 16 pieces of 16 bytes over 512 lanes: lanes 16 j .. 16 j + 15 write one row
+  {
+    OutT* out = reinterpret_cast<OutT*>(P.out);
+    const int64_t rbase = (int64_t)qb * kBlk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * 512 + (int)threadIdx.x;
+      const int r = q >> 4, ch = q & 15;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + r * kStgPitch + ch * 16);
+      *reinterpret_cast<u32x4*>(out + (rbase + r) * ((int64_t)P.hq * D) + (int64_t)h * D + ch * 8) = val;
+    }
+  }
 }
 
 template <int D, typename OutT, bool VARLEN>
