@@ -6,11 +6,16 @@
 // .compute_chunked_prefill: the history segment is attended without the
 // causal rule, the chunk's own keys with it, and each part returns (out, lse).
 //
-// Kernel design (gfx950):
+// Two kernels (gfx950).  bsa3_kernel (bf16, head_dim 128; the hot path) is
+// described above its body below: two groups of four waves alternate matrix
+// and vector phases on alternate kept blocks of one (query head, query block).
+// bsa_kernel (XA_F32 inputs, head_dim 64, and tiles whose offsets exceed 32
+// bits):
 //   * one workgroup = one (query head, 128-row query block); 8 waves.  Wave w
 //     owns query rows 32*(w%4) .. +32 and key half 64*(w/4) .. +64 of every
 //     kept key block (split over keys inside the workgroup; the two halves are
 //     merged once at the end through LDS);
+// Both:
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     a lane then owns one query row and 16 keys, so the row max / row sum are
 //     mostly in-lane (one cross-half exchange per block for the max);
@@ -18,8 +23,8 @@
 //     directly the B operand of the O^T += V^T P^T MFMA; V is stored transposed
 //     in the workspace with the matching key order inside each 16-key group,
 //     so both operands come from LDS with 16-byte reads;
-//   * K and V^T tiles of the next kept block are fetched into registers while
-//     the current one is being multiplied (two LDS buffers);
+//   * (bsa_kernel) K and V^T tiles of the next kept block are fetched into
+//     registers while the current one is being multiplied (two LDS buffers);
 //   * the walk over key blocks touches only kept blocks, in ascending order,
 //     from a list built in LDS from the mask row.
 // XA_F32 inputs use bf16 hi/lo planes and three MFMAs per product.
@@ -36,10 +41,12 @@ constexpr int kBlk = 128;
 constexpr int kThreads = 512;
 constexpr int kListMax = 1024;
 
-// Work order: clusters of (kv head, query block), heaviest query blocks first;
-// the `group` query heads of a cluster get consecutive dispatch slots on the
-// same XCD (ids b, b+8, b+16, ...), so they read the same K/V tiles through
-// one L2.
+// Item index -> (query head, query block): clusters of (kv head, query block),
+// the last query blocks (the most keys under the causal rule) first, the
+// `group` query heads of a cluster at ids b, b+8, b+16, ...  Without a work
+// order the ids are dispatch slots (workgroup b runs on XCD b mod 8, so a
+// cluster's heads share one L2); with one, the order's tickets decide which
+// workgroup runs an item and this map only names the items.
 __device__ __forceinline__ void bsa_decode(int bid, int group, int hkv, int n_qb, int& h, int& qb) {
   const int clusters = hkv * n_qb;
   const int full_rounds = clusters / 8;
