@@ -406,11 +406,11 @@ def measure(a, w, q, k, v, fused=None):
         run.run()
     torch.cuda.synchronize()
 
-    # timed region, with events around every library call; the events are created beforehand (creating one
-    # inside the timed region can stall the host for tens of milliseconds)
+    from block_sparse_attention_xattn_amd import binding as B
     stream = torch.cuda.current_stream()
     ev = []
-    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(12 * len(run.bufs) * a.steps + 8)]
+    # events are created before they are needed (creating one mid-run can stall the host)
+    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(24 * len(run.bufs) * a.steps + 16)]
 
     def mark(tag):
         e = ev_pool.pop() if ev_pool else torch.cuda.Event(enable_timing=True)
@@ -418,17 +418,7 @@ def measure(a, w, q, k, v, fused=None):
         ev.append((tag, e))
 
     orig_est, orig_merge, orig_pack, orig_reduce = run.estimate, run.merge, run.pack, run.reduce
-
-    def timed(tag, fn):
-        def inner(b):
-            mark(tag + ":start")
-            fn(b)
-            mark(tag + ":end")
-        return inner
-
-    from block_sparse_attention_xattn_amd import binding as B
-    orig_bsa = B.bsa_prefill_packed
-    orig_seg = B.bsa_prefill_segments
+    orig_bsa, orig_seg = B.bsa_prefill_packed, B.bsa_prefill_segments
 
     def wrap(fn):
         def inner(*args, **kw):
@@ -438,13 +428,16 @@ def measure(a, w, q, k, v, fused=None):
             return r
         return inner
 
-    run.estimate = timed("estimate", orig_est)
-    if not run.fused:
-        run.merge = timed("merge", orig_merge)
-    run.pack = timed("pack", orig_pack)
-    run.reduce = timed("reduce", orig_reduce)
-    B.bsa_prefill_packed = wrap(orig_bsa)
-    B.bsa_prefill_segments = wrap(orig_seg)
+    def timed(tag, fn):
+        def inner(b):
+            mark(tag + ":start")
+            fn(b)
+            mark(tag + ":end")
+        return inner
+
+    # timed region: a.steps steps with events only around each attention call (each recorded event leaves the
+    # GPU idle for a few microseconds between calls)
+    B.bsa_prefill_packed, B.bsa_prefill_segments = wrap(orig_bsa), wrap(orig_seg)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -455,10 +448,20 @@ def measure(a, w, q, k, v, fused=None):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    B.bsa_prefill_packed = orig_bsa
-    B.bsa_prefill_segments = orig_seg
+    B.bsa_prefill_packed, B.bsa_prefill_segments = orig_bsa, orig_seg
     gpu_ms = e0.elapsed_time(e1)
     step_ms = max(gpu_ms, wall * 1e3) / a.steps
+
+    # then, untimed, the same steps with events around the other calls too, for their part of a step
+    run.estimate = timed("estimate", orig_est)
+    if not run.fused:
+        run.merge = timed("merge", orig_merge)
+    run.pack = timed("pack", orig_pack)
+    run.reduce = timed("reduce", orig_reduce)
+    for _ in range(a.steps):
+        run.run()
+    torch.cuda.synchronize()
+    run.estimate, run.merge, run.pack, run.reduce = orig_est, orig_merge, orig_pack, orig_reduce
 
     parts = {}
     bsa_durs = []
