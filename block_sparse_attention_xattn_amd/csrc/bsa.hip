@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float ref = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - ref);
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void bsa_kernel(BsaParams P) {
   }
 
   // ---- merge the two key halves of each query row, normalise, write
-  const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float l_row = halves_sum(l_run);
   float* xch = reinterpret_cast<float*>(smem);  // [4][NMD*16 + 2][64]
   constexpr int XV = NMD * 16 + 2;
   if (wk == 1) {
@@ -631,7 +631,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = halves_max(mx);
         const bool upd = mx > m_run && (m_run == -INFINITY || (mx - m_run) * c > kRescale);
         if (__builtin_amdgcn_ballot_w64(upd)) {
           const float m_new = upd ? mx : m_run;
@@ -709,7 +709,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     m_run = m;
   }
 
-  const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float l_row = halves_sum(l_run);
   float inv = 0.f, lse_v = -INFINITY;
   if (l_row > 0.f) {
     inv = 1.f / l_row;

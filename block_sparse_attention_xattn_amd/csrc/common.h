@@ -33,6 +33,19 @@ __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combination of lane l's value with lane l^32's (the two 32-lane halves of a wave).  v_permlane32_swap
+// exchanges the halves in one VALU instruction, where a shuffle would make a round trip through the LDS
+// unit; called with the same register twice it hands every lane the pair {x_l, x_(l^32)}, so both
+// halves compute the same result.  All 64 lanes must be active.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // fp32 -> (hi, lo) bf16 pair with hi + lo ~= x to about 16 mantissa bits.
 __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
   hi = (bf16)x;

@@ -142,12 +142,12 @@ __global__ __launch_bounds__(kEThreads) void est_gemm_kernel(EstParams P) {
       float mx = -INFINITY;
 #pragma unroll
       for (int v = g0; v < g0 + HALF; ++v) mx = fmaxf(mx, x[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = halves_max(mx);
       float s = 0.f;
       const float ref = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
       for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(x[v] - ref);
-      s += __shfl_xor(s, 32);
+      s = halves_sum(s);
       const int kb = w_c0 / (2 * HALF) + g0 / HALF;
       if (hh == 0 && r < P.R && kb < P.nkb)
         P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kb) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
@@ -282,32 +282,40 @@ __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
   }
   if (!wave_live) return;
 
+  // every column of the wave valid for every row of it: no per-element mask
+  const bool full = w_c0 + 63 < P.N && (int64_t)w_c0 + 63 <= cdiag + w_r0;
+  const float sc = P.scale_log2;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int r = w_r0 + nt * 32 + n;
-    float x[32];
+    float x[32];  // raw scores (the scale is positive, so the maximum is taken before scaling)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-        const bool ok = c < P.N && c <= cdiag + r;
-        x[mt * 16 + i] = ok ? acc[mt][nt][i] * P.scale_log2 : -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i) x[mt * 16 + i] = acc[mt][nt][i];
+    if (!full) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+          if (!(c < P.N && c <= cdiag + r)) x[mt * 16 + i] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int g0 = 0; g0 < 32; g0 += HALF) {
       float mx = -INFINITY;
 #pragma unroll
       for (int v = g0; v < g0 + HALF; ++v) mx = fmaxf(mx, x[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = halves_max(mx);
+      const float ref = mx == -INFINITY ? 0.f : mx * sc;
       float s = 0.f;
-      const float ref = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
-      for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(x[v] - ref);
-      s += __shfl_xor(s, 32);
+      for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(__builtin_fmaf(x[v], sc, -ref));
+      s = halves_sum(s);
       const int kbk = w_c0 / (2 * HALF) + g0 / HALF;
       if (hh == 0 && r < P.R && kbk < P.nkb)
-        P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : mx + log2f(s);
+        P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : ref + log2f(s);
     }
   }
 }
