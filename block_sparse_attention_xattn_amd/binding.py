@@ -47,6 +47,8 @@ def _declare(lib):
     lib.xattn_last_error.argtypes = []
     lib.xattn_version.restype = ctypes.c_char_p
     lib.xattn_version.argtypes = []
+    lib.xattn_set_attention_events.restype = ctypes.c_int
+    lib.xattn_set_attention_events.argtypes = [P, P]
     lib.xattn_estimate_workspace_size.restype = SZ
     lib.xattn_estimate_workspace_size.argtypes = [I64, I64, I32, I32, I32, I32, I32, ctypes.c_int]
     lib.xattn_estimate.restype = ctypes.c_int
@@ -142,6 +144,19 @@ def _qkv_check(t: torch.Tensor, name: str):
         raise XattnError(XA_EINVAL, f"{name} must be a GPU tensor")
     if t.dim() != 3 or t.stride(2) != 1:
         raise XattnError(XA_EINVAL, f"{name} must be [tokens, heads, head_dim] with a contiguous last dim")
+
+
+def xattn_set_attention_events(before=None, after=None, stream=None):
+    """Measurement hook: later attention calls on this thread record the torch.cuda.Event objects
+    `before` / `after` immediately around each launch of the ping-pong attention kernel; (None, None)
+    turns it off.  An event torch has not created yet is recorded once on `stream` here so that its
+    handle exists."""
+    handles = []
+    for ev in (before, after):
+        if ev is not None and ev.cuda_event == 0:
+            ev.record(torch.cuda.current_stream() if stream is None else stream)
+        handles.append(None if ev is None else ctypes.c_void_p(ev.cuda_event))
+    _check(lib().xattn_set_attention_events(*handles))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

@@ -45,6 +45,13 @@ using xa_host::fail;
 extern "C" const char* xattn_last_error(void) { return xa_host::g_err; }
 extern "C" const char* xattn_version(void) { return "xattn-gfx950 0.1"; }
 
+extern "C" xa_status_t xattn_set_attention_events(xa_event_t before, xa_event_t after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(XA_EINVAL, "xattn_set_attention_events: pass both events or neither");
+  set_attention_events(reinterpret_cast<hipEvent_t>(before), reinterpret_cast<hipEvent_t>(after));
+  return XA_OK;
+}
+
 // ---------------------------------------------------------------------------
 // shared validation
 // ---------------------------------------------------------------------------

@@ -1152,6 +1152,15 @@ static bool tile_offsets_fit(const BsaParams* segs, int n_seg, int D) {
   return true;
 }
 
+static thread_local hipEvent_t t_attn_events[2] = {nullptr, nullptr};
+void set_attention_events(hipEvent_t before, hipEvent_t after) {
+  t_attn_events[0] = before;
+  t_attn_events[1] = after;
+}
+static hipError_t record_attention_event(int k, hipStream_t s) {
+  return t_attn_events[k] ? hipEventRecord(t_attn_events[k], s) : hipSuccess;
+}
+
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s) {
   if constexpr (!SPLIT && D == 128) {
@@ -1181,7 +1190,10 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
           m.part_lse = plan->part_lse;
           grid = total + plan->max_split;  // entries: items plus halves of split items
         }
+        hipError_t ev = record_attention_event(0, s);
+        if (ev != hipSuccess) return ev;
         hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
+        if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
         if (plan && plan->max_split > 0)
           hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(plan->max_split, 64)), dim3(256), 0, s,
                              m);
@@ -1215,7 +1227,10 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   m.split_items = plan->split_items;
   m.part_o = plan->part_o;
   m.part_lse = plan->part_lse;
+  hipError_t ev = record_attention_event(0, s);
+  if (ev != hipSuccess) return ev;
   hipLaunchKernelGGL((bsa3_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(512), 0, s, m);
+  if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
   if (plan->max_split > 0)
     hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
   return hipGetLastError();

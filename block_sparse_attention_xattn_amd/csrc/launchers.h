@@ -135,6 +135,10 @@ inline BsaPlanLayout bsa_plan_layout(int64_t n_items, int d) {
   return L;
 }
 
+// Events recorded on the launch stream immediately before / after each launch of the ping-pong attention
+// kernel (both null: none); per host thread, the events belong to the caller.
+void set_attention_events(hipEvent_t before, hipEvent_t after);
+
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hipStream_t s);
 // A packed batch of bf16, head_dim 128 sequences (records seqs in device memory, n_items = hq * total

@@ -27,7 +27,8 @@
  *     xattn_last_error() returns a thread-local message.  XA_EHIP means a
  *     launch failed (hipGetLastError); outputs are then undefined.
  *   - Batch = 1 per call (one sequence), as the policy on the pages does.
- *   - Thread-safe: no global mutable state besides the thread-local message.
+ *   - Thread-safe: no global mutable state besides the thread-local message
+ *     and the thread-local measurement events (xattn_set_attention_events).
  */
 #ifndef XATTN_H_
 #define XATTN_H_
@@ -40,6 +41,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* xa_stream_t; /* a hipStream_t */
+typedef struct ihipEvent_t* xa_event_t;   /* a hipEvent_t */
 
 typedef enum {
   XA_OK = 0,
@@ -56,6 +58,20 @@ const char* xattn_last_error(void);
 
 /* Library version string (static storage). */
 const char* xattn_version(void);
+
+/* Measurement hook, not a step of the method.  While set, every call that
+ * launches the ping-pong attention kernel (head_dim 128: bsa_prefill,
+ * bsa_prefill_packed, bsa_prefill_segments, bsa_prefill_varlen,
+ * bsa_history_offloaded) records `before` on its stream immediately before
+ * that launch and `after` immediately after it, so hipEventElapsedTime gives
+ * the attention kernel alone, without the work-order kernels and the merge of
+ * split halves the call also enqueues.  A call with several such launches
+ * (bsa_history_offloaded, one per ring group) leaves the last one in the
+ * events.  Both NULL switches the hook off; exactly one NULL is XA_EINVAL.
+ * The events are the caller's (hipEventCreate'd, valid while set); the
+ * setting belongs to the calling host thread.  A failed record makes the
+ * attention call return XA_EHIP. */
+xa_status_t xattn_set_attention_events(xa_event_t before, xa_event_t after);
 
 /* ------------------------------------------------------------------------
  * Part 1: importance estimate + block selection  (xattn_estimate_chunked)

@@ -116,6 +116,14 @@ def test_bsa_packed_rejects(lib, over, status):
     assert _bsa_packed(lib, **over) == status
 
 
+def test_attention_events_arguments(lib):
+    # exactly one event is an error; both null switches the hook off (no HIP call is made either way)
+    assert lib.xattn_set_attention_events(None, FAKE) == B.XA_EINVAL
+    assert lib.xattn_set_attention_events(FAKE, None) == B.XA_EINVAL
+    assert b"both events or neither" in lib.xattn_last_error()
+    assert lib.xattn_set_attention_events(None, None) == B.XA_OK
+
+
 def test_merge_and_reducer_reject(lib):
     P = ctypes.c_void_p
     assert lib.attn_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B.XA_BF16, 128, 4, 100, None) == B.XA_EINVAL

@@ -251,6 +251,44 @@ def test_segments_in_one_launch():
         PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
 
 
+def test_attention_event_hook():
+    """The measurement hook: the events land around the attention kernel, inside the call's own interval,
+    and the results are the same as without them."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, L, p = 8, 2, 128, 1280, 768
+    qd, kd, vd = (_rand((L, h, d), torch.bfloat16, 90 + i).to(DEV) for i, h in enumerate((hq, hkv, hkv)))
+    packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
+    B.bsa_pack_v(vd, packed, 0)
+    md = torch.from_numpy((np.random.default_rng(3).random((hq, (L - p) // 128, L // 128)) < 0.5)
+                          .astype(np.uint8)).to(DEV)
+
+    def call():
+        outs = [(torch.empty(L - p, hq, d, dtype=torch.float32, device=DEV),
+                 torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(2)]
+        segs = [dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=md, causal=False,
+                     out=outs[0][0], lse=outs[0][1]),
+                dict(k=kd[p:], kv_start=p, v_token_offset=p, block_mask=md, causal=True,
+                     out=outs[1][0], lse=outs[1][1])]
+        B.bsa_prefill_segments(qd[p:], packed, p, segs)
+        return outs
+
+    plain = call()
+    c0, c1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    c0.record()
+    try:
+        B.xattn_set_attention_events(k0, k1)
+        hooked = call()
+    finally:
+        B.xattn_set_attention_events(None, None)
+    c1.record()
+    torch.cuda.synchronize()
+    t_call, t_kernel = c0.elapsed_time(c1), k0.elapsed_time(k1)
+    assert 0.0 < t_kernel <= t_call
+    assert c0.elapsed_time(k0) >= 0.0 and k1.elapsed_time(c1) >= 0.0
+    for (a, b), (x, y) in zip(plain, hooked):
+        assert torch.equal(a, x) and torch.equal(b, y)
+
+
 def test_segments_work_order():
     """The work order of a segmented launch, read back from its workspace.
 
