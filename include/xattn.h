@@ -60,10 +60,12 @@ const char* xattn_last_error(void);
 const char* xattn_version(void);
 
 /* Measurement hook, not a step of the method.  While set, every call that
- * launches the ping-pong attention kernel (head_dim 128: bsa_prefill,
- * bsa_prefill_packed, bsa_prefill_segments, bsa_prefill_varlen,
- * bsa_history_offloaded) records `before` on its stream immediately before
- * that launch and `after` immediately after it, so hipEventElapsedTime gives
+ * launches the ping-pong attention kernel (bf16 inputs with head_dim 128
+ * through bsa_prefill, bsa_prefill_packed, bsa_prefill_segments,
+ * bsa_prefill_varlen or bsa_history_offloaded; fp32 inputs and other head
+ * dims run another kernel and record nothing) records `before` on its stream
+ * immediately before that launch and `after` immediately after it, so
+ * hipEventElapsedTime gives
  * the attention kernel alone, without the work-order kernels and the merge of
  * split halves the call also enqueues.  A call with several such launches
  * (bsa_history_offloaded, one per ring group) leaves the last one in the
