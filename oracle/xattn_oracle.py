@@ -508,6 +508,36 @@ def density(mask, q_start_pos: int, block: int = 128) -> float:
     return float((mask & causal[None]).sum()) / float(causal.sum() * H)
 
 
+def density_counts(mask) -> tuple[int, int]:
+    """(selected, total) block counts of one chunk's mask, as integers.
+
+    XAttentionBSAPolicy ``select_blocks`` step 5: the mask is [H, valid query
+    blocks, valid key blocks]; the query blocks sit at the end of the keys
+    (offset = key blocks - query blocks), a (query block, key block) pair is
+    causal iff its key block is at most the query block plus that offset; the
+    total is the causal pair count times the head count, the selected count the
+    mask's kept pairs among them.
+    """
+    mask = np.asarray(mask).astype(bool)
+    H, nQB, nKB = mask.shape
+    q_offset = nKB - nQB
+    causal = np.arange(nKB)[None, :] <= (np.arange(nQB)[:, None] + q_offset)
+    total = int(causal.sum()) * H
+    selected = int((mask & causal[None]).sum())
+    return selected, total
+
+
+def comm_density_counts(keep_any) -> tuple[int, int]:
+    """(selected, available) cache-block counts of one chunk.
+
+    XAttentionBSAPolicy ``select_blocks`` after step 6: the cache blocks to
+    load (the union keep list, first and last already forced) over the cache
+    blocks the history holds.
+    """
+    keep_any = np.asarray(keep_any).astype(bool)
+    return int(keep_any.sum()), int(keep_any.size)
+
+
 # ---------------------------------------------------------------------------
 # Next step: the estimate against downsampled history keys (metadata of
 # offloaded K)
