@@ -103,6 +103,8 @@ def _declare(lib):
     lib.attn_merge.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I32, I32, P]
     lib.xattn_mask_to_cache_blocks.restype = ctypes.c_int
     lib.xattn_mask_to_cache_blocks.argtypes = [P, I32, I32, I64, I64, I64, I64, I64, I32, I32, P, P, P, P]
+    lib.xattn_density_counts.restype = ctypes.c_int
+    lib.xattn_density_counts.argtypes = [P, I32, I32, I64, I64, I64, I64, P, I64, P, P]
     return lib
 
 
@@ -144,6 +146,78 @@ def _qkv_check(t: torch.Tensor, name: str):
         raise XattnError(XA_EINVAL, f"{name} must be a GPU tensor")
     if t.dim() != 3 or t.stride(2) != 1:
         raise XattnError(XA_EINVAL, f"{name} must be [tokens, heads, head_dim] with a contiguous last dim")
+
+
+def _dense_check(t, name: str, shape, dtype, device):
+    """t must be a contiguous tensor of exactly `shape` and `dtype` on `device` (the kernels write it densely)."""
+    if t is None:
+        return
+    if not t.is_cuda or t.device != torch.device(device):
+        raise XattnError(XA_EINVAL, f"{name} must be on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise XattnError(XA_EINVAL, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise XattnError(XA_EINVAL, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise XattnError(XA_EINVAL, f"{name} must be contiguous")
+
+
+def _flat_check(t, name: str, min_elems: int, dtype, device):
+    """t must be a contiguous tensor of `dtype` on `device` holding at least min_elems elements."""
+    if not t.is_cuda or t.device != torch.device(device):
+        raise XattnError(XA_EINVAL, f"{name} must be on {device}")
+    if t.dtype != dtype or not t.is_contiguous():
+        raise XattnError(XA_EINVAL, f"{name} must be a contiguous {dtype} tensor")
+    if t.numel() < min_elems:
+        raise XattnError(XA_EINVAL, f"{name} holds {t.numel()} elements, needs {min_elems}")
+
+
+def _mask_check(m, name: str, device, heads=None, n_rows=None, col_lo=None, col_hi=None, hs=None, rs=None):
+    """A byte mask on `device` with a contiguous last dim; when the rows / columns a call reads are given,
+    every byte h*hs + qb*rs + col (h < heads, qb < n_rows, col_lo <= col <= col_hi) must lie inside the
+    tensor's storage."""
+    if not m.is_cuda or m.device != torch.device(device):
+        raise XattnError(XA_EINVAL, f"{name} must be on {device}")
+    if m.dtype not in (torch.uint8, torch.bool) or m.stride(-1) not in (0, 1):
+        raise XattnError(XA_EINVAL, f"{name} must be uint8/bool with a contiguous last dim")
+    if heads is None or n_rows is None or col_hi is None or col_hi < col_lo:
+        return
+    hs = m.stride(0) if hs is None else hs
+    rs = m.stride(1) if rs is None else rs
+    if col_lo < 0 or hs < 0 or rs < 0:
+        raise XattnError(XA_EINVAL, f"{name}: negative column or stride")
+    last = (heads - 1) * hs + (n_rows - 1) * rs + col_hi
+    avail = m.untyped_storage().nbytes() - m.storage_offset() * m.element_size()
+    if last >= avail:
+        raise XattnError(XA_EINVAL, f"{name}: the call reads byte {last} but only {avail} are reachable")
+
+
+def _out_dtype(out, out_dtype, default):
+    """The output dtype: out_dtype if given, else out's, else default; out must agree with it."""
+    odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else default)
+    if out is not None and out.dtype != odt:
+        raise XattnError(XA_EINVAL, f"out has dtype {out.dtype} but out_dtype is {odt}")
+    return odt
+
+
+def _attn_mask_strides(m, q, hq, q_len, kv_start, kv_len, mask_kb_offset, block, mask_head_stride,
+                       mask_row_stride):
+    """(head stride, row stride) of an attention call's mask after checking that every byte the call reads
+    (heads 0..hq-1, query blocks 0..q_len/block-1, the key blocks of [kv_start, kv_start+kv_len) shifted by
+    mask_kb_offset) lies inside it; (0, 0) without a mask."""
+    if m is None:
+        return 0, 0
+    if m.dim() != 3:
+        raise XattnError(XA_EINVAL, "block_mask must be [heads, query blocks, key blocks] (or a broadcast view)")
+    hs = m.stride(0) if mask_head_stride is None else mask_head_stride
+    rs = m.stride(1) if mask_row_stride is None else mask_row_stride
+    if kv_len > 0 and q_len > 0:
+        lo = kv_start // block - mask_kb_offset
+        hi = (kv_start + kv_len - 1) // block - mask_kb_offset
+        _mask_check(m, "block_mask", q.device, hq, max(q_len // block, 1), lo, hi, hs, rs)
+    else:
+        _mask_check(m, "block_mask", q.device)
+    return hs, rs
 
 
 def xattn_set_attention_events(before=None, after=None, stream=None):
@@ -189,6 +263,9 @@ def xattn_estimate(q, k, q_start_pos: int, stride: int = 8, threshold: float = 0
         block_scores = torch.empty(hq, n_qb, nkb, dtype=torch.float32, device=q.device)
     if block_mask is None:
         block_mask = torch.empty(hq, n_qb, nkb, dtype=torch.uint8, device=q.device)
+    _dense_check(block_scores, "block_scores", (hq, n_qb, nkb), torch.float32, q.device)
+    _dense_check(block_mask, "block_mask", (hq, n_qb, nkb), block_mask.dtype if block_mask.dtype == torch.bool
+                 else torch.uint8, q.device)
     need = xattn_estimate_workspace_size(q_len, k_len, hq, hkv, d, stride, block, dt)
     if ws is None:
         ws = workspace(need, q.device)
@@ -212,19 +289,16 @@ def bsa_prefill(q, k, v, q_start_pos: int, kv_start: int, block_mask=None, mask_
         raise XattnError(XA_EINVAL, "q, k, v dtypes differ")
     q_len, hq, d = q.shape
     kv_len, hkv, _ = k.shape
-    if out_dtype is None:
-        out_dtype = q.dtype
+    out_dtype = _out_dtype(out, out_dtype, q.dtype)
     odt = _dtype_code(torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty(q_len, hq, d, dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty(hq, q_len, dtype=torch.float32, device=q.device)
-    hs = rs = 0
-    if block_mask is not None:
-        if block_mask.dtype not in (torch.uint8, torch.bool) or block_mask.stride(-1) != 1:
-            raise XattnError(XA_EINVAL, "block_mask must be uint8/bool with a contiguous last dim")
-        hs = block_mask.stride(0) if mask_head_stride is None else mask_head_stride
-        rs = block_mask.stride(1) if mask_row_stride is None else mask_row_stride
+    _dense_check(out, "out", (q_len, hq, d), out_dtype, q.device)
+    _dense_check(lse, "lse", (hq, q_len), torch.float32, q.device)
+    hs, rs = _attn_mask_strides(block_mask, q, hq, q_len, kv_start, kv_len, mask_kb_offset, block,
+                                mask_head_stride, mask_row_stride)
     need = bsa_prefill_workspace_size(q_len, kv_len, hq, hkv, d, dt)
     if ws is None:
         ws = workspace(need, q.device)
@@ -274,17 +348,16 @@ def bsa_prefill_packed(q, k, packed: PackedV, v_token_offset: int, q_start_pos: 
     dt = _dtype_code(q)
     q_len, hq, d = q.shape
     kv_len, hkv, _ = k.shape
-    if out_dtype is None:
-        out_dtype = q.dtype
+    out_dtype = _out_dtype(out, out_dtype, q.dtype)
     odt = _dtype_code(torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty(q_len, hq, d, dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty(hq, q_len, dtype=torch.float32, device=q.device)
-    hs = rs = 0
-    if block_mask is not None:
-        hs = block_mask.stride(0) if mask_head_stride is None else mask_head_stride
-        rs = block_mask.stride(1) if mask_row_stride is None else mask_row_stride
+    _dense_check(out, "out", (q_len, hq, d), out_dtype, q.device)
+    _dense_check(lse, "lse", (hq, q_len), torch.float32, q.device)
+    hs, rs = _attn_mask_strides(block_mask, q, hq, q_len, kv_start, kv_len, mask_kb_offset, block,
+                                mask_head_stride, mask_row_stride)
     need = bsa_prefill_packed_workspace_size(q_len, kv_len, hq, hkv, d, dt)
     if ws is None and need > 0:
         ws = workspace(need, q.device)
@@ -313,12 +386,19 @@ def bsa_prefill_segments(q, packed: PackedV, q_start_pos: int, segments, softmax
     q_len, hq, d = q.shape
     arr = (Segment * len(segments))()
     keep = []
+    if not segments:
+        raise XattnError(XA_EINVAL, "bsa_prefill_segments: no segments")
+    out_dtype = segments[0]["out"].dtype
     for i, g in enumerate(segments):
         k = g["k"]
         _qkv_check(k, "k")
+        if k.device != q.device or k.dtype != q.dtype:
+            raise XattnError(XA_EINVAL, f"segment {i}: k must be on q's device with q's dtype")
+        _dense_check(g["out"], f"segment {i} out", (q_len, hq, d), out_dtype, q.device)
+        _dense_check(g["lse"], f"segment {i} lse", (hq, q_len), torch.float32, q.device)
         m = g.get("block_mask")
-        hs = g.get("mask_head_stride", m.stride(0) if m is not None else 0)
-        rs = g.get("mask_row_stride", m.stride(1) if m is not None else 0)
+        hs, rs = _attn_mask_strides(m, q, hq, q_len, g["kv_start"], k.shape[0], g.get("mask_kb_offset", 0), block,
+                                    g.get("mask_head_stride"), g.get("mask_row_stride"))
         arr[i] = Segment(k.data_ptr(), k.stride(0), k.stride(1), k.shape[0], g["kv_start"], g["v_token_offset"],
                          None if m is None else m.data_ptr(), hs, rs, g.get("mask_kb_offset", 0),
                          1 if g["causal"] else 0, g["out"].data_ptr(), g["lse"].data_ptr())
@@ -362,6 +442,8 @@ def xattn_estimate_history_ds(q, k_ds, stride: int, threshold: float, block: int
         block_scores = torch.empty(hq, q_len // b, n_ds // b, dtype=torch.float32, device=q.device)
     if block_mask is None:
         block_mask = torch.empty(hq, q_len // b, n_ds // b, dtype=torch.uint8, device=q.device)
+    _dense_check(block_scores, "block_scores", (hq, q_len // b, n_ds // b), torch.float32, q.device)
+    _dense_check(block_mask, "block_mask", (hq, q_len // b, n_ds // b), torch.uint8, q.device)
     if ws is None:
         ws = workspace(xattn_estimate_history_ds_workspace_size(q_len, n_ds, hq, hkv, d, stride, block, dt),
                        q.device)
@@ -412,6 +494,12 @@ def bsa_history_offloaded(q, q_start_pos: int, store: OffloadedKV, keep, out, ls
     """Attention of q over the host cache blocks `keep` (ids, no causal rule) through the ring (see xattn.h)."""
     _qkv_check(q, "q")
     q_len, hq, d = q.shape
+    for t, nm in ((out, "out"), (part_out, "part_out")):
+        _dense_check(t, nm, (q_len, hq, d), torch.bfloat16, q.device)
+    for t, nm in ((lse, "lse"), (part_lse, "part_lse")):
+        _dense_check(t, nm, (hq, q_len), torch.float32, q.device)
+    if any(int(i) < 0 or int(i) >= store.n_blocks for i in keep):
+        raise XattnError(XA_EINVAL, "keep ids must lie in the host store")
     ids = (ctypes.c_int32 * max(len(keep), 1))(*[int(i) for i in keep])
     _check(lib().bsa_history_offloaded(_ptr(q), q.stride(0), q.stride(1), _dtype_code(q), q_len, hq, store.hkv, d,
                                        q_start_pos, ctypes.c_void_p(store.host_k.data_ptr()),
@@ -507,6 +595,8 @@ def xattn_estimate_varlen(q, k, cu_seqlens_q, cu_seqlens_k, stride: int = 8, thr
         block_scores = torch.empty(max(n, 1), dtype=torch.float32, device=q.device)
     if block_mask is None:
         block_mask = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _flat_check(block_scores, "block_scores", n, torch.float32, q.device)
+    _flat_check(block_mask, "block_mask", n, torch.uint8, q.device)
     if ws is None:
         ws = workspace(lib().xattn_estimate_varlen_workspace_size(cq, ck, b, hq, hkv, stride), q.device)
     _check(lib().xattn_estimate_varlen(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
@@ -524,11 +614,16 @@ def bsa_prefill_varlen(q, k, packed: PackedV, cu_seqlens_q, cu_seqlens_k, block_
     hkv = k.shape[1]
     cq, b = _cu(cu_seqlens_q)
     ck, _ = _cu(cu_seqlens_k)
-    odt = q.dtype if out_dtype is None else out_dtype
+    odt = _out_dtype(out, out_dtype, q.dtype)
     if out is None:
         out = torch.empty(total_q, hq, d, dtype=odt, device=q.device)
     if lse is None:
         lse = torch.empty(max(hq * total_q, 1), dtype=torch.float32, device=q.device)
+    _dense_check(out, "out", (total_q, hq, d), odt, q.device)
+    _flat_check(lse, "lse", hq * total_q, torch.float32, q.device)
+    if block_mask is not None:
+        _flat_check(block_mask, "block_mask", int(lib().xattn_varlen_mask_elems(cq, ck, b, hq)),
+                    block_mask.dtype if block_mask.dtype == torch.bool else torch.uint8, q.device)
     if ws is None:
         ws = workspace(lib().bsa_prefill_varlen_workspace_size(cq, ck, b, hq, d), q.device)
     _check(lib().bsa_prefill_varlen(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
@@ -541,14 +636,17 @@ def bsa_prefill_varlen(q, k, packed: PackedV, cu_seqlens_q, cu_seqlens_k, block_
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
     """LSE merge (see xattn.h); o_out / lse_out may alias the inputs.  Returns (o, lse)."""
+    if o_a.dim() != 3:
+        raise XattnError(XA_EINVAL, "attn_merge: o_a must be [q_len, heads, head_dim]")
     q_len, heads, d = o_a.shape
-    for t in (o_a, o_b, lse_a, lse_b):
-        if not t.is_cuda or not t.is_contiguous():
-            raise XattnError(XA_EINVAL, "attn_merge needs contiguous GPU tensors")
     if o_out is None:
         o_out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    for t, nm in ((o_a, "o_a"), (o_b, "o_b"), (o_out, "o_out")):
+        _dense_check(t, nm, (q_len, heads, d), o_a.dtype, o_a.device)
+    for t, nm in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse_out, "lse_out")):
+        _dense_check(t, nm, (heads, q_len), torch.float32, o_a.device)
     _check(lib().attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out), _ptr(lse_out),
                             _dtype_code(o_a), q_len, heads, d, _stream(stream)))
     return o_out, lse_out
@@ -560,14 +658,43 @@ def xattn_mask_to_cache_blocks(block_mask, kb_begin: int, n_cache_blocks: int, s
     """Reduce a [H, n_qb, n_cols] block mask to cache blocks.  Returns (per_head, any, any_blocks)."""
     H, n_qb, n_cols = block_mask.shape
     dev = block_mask.device
+    _mask_check(block_mask, "block_mask", dev, H, n_qb, 0, n_cols - 1)
     if keep_per_head is None and "per_head" in want:
         keep_per_head = torch.empty(H, n_qb, n_cache_blocks, dtype=torch.uint8, device=dev)
     if keep_any is None and "any" in want:
         keep_any = torch.empty(n_cache_blocks, dtype=torch.uint8, device=dev)
     if keep_any_blocks is None and "any_blocks" in want:
         keep_any_blocks = torch.empty(n_cache_blocks * sub_blocks, dtype=torch.uint8, device=dev)
+    _dense_check(keep_per_head, "keep_per_head", (H, n_qb, n_cache_blocks), torch.uint8, dev)
+    _dense_check(keep_any, "keep_any", (n_cache_blocks,), torch.uint8, dev)
+    _dense_check(keep_any_blocks, "keep_any_blocks", (n_cache_blocks * sub_blocks,), torch.uint8, dev)
     _check(lib().xattn_mask_to_cache_blocks(_ptr(block_mask), H, n_qb, n_cols, block_mask.stride(0),
                                             block_mask.stride(1), kb_begin, n_cache_blocks, sub_blocks,
                                             1 if force_first_last else 0, _ptr(keep_per_head), _ptr(keep_any),
                                             _ptr(keep_any_blocks), _stream(stream)))
     return keep_per_head, keep_any, keep_any_blocks
+
+
+def xattn_density_counts(counts, block_mask=None, diag0: int = 0, keep_any=None, stream=None):
+    """Add a chunk's density counts to `counts` (int64 [4] on the GPU; see xattn.h):
+    [kept causal pairs, causal pairs, kept cache blocks, cache blocks].
+
+    block_mask: [H, n_qb, n_cols] uint8 (query block qb's causal columns are 0 .. diag0 + qb), or None;
+    keep_any: [n_cache_blocks] uint8, or None.  Returns counts.
+    """
+    if not counts.is_cuda or counts.dtype != torch.int64 or counts.numel() < 4 or not counts.is_contiguous():
+        raise XattnError(XA_EINVAL, "counts must be a contiguous int64 GPU tensor of at least 4 elements")
+    H = n_qb = n_cols = hs = rs = 0
+    if block_mask is not None:
+        _mask_check(block_mask, "block_mask", counts.device)
+        H, n_qb, n_cols = block_mask.shape
+        hs, rs = block_mask.stride(0), block_mask.stride(1)
+    ncb = 0
+    if keep_any is not None:
+        if not keep_any.is_cuda or keep_any.dtype not in (torch.uint8, torch.bool) or not keep_any.is_contiguous():
+            raise XattnError(XA_EINVAL, "keep_any must be a contiguous uint8/bool GPU tensor")
+        ncb = keep_any.numel()
+    _check(lib().xattn_density_counts(_ptr(block_mask), H, n_qb, n_cols, hs, rs, diag0, _ptr(keep_any), ncb,
+                                      _ptr(counts), _stream(stream)))
+    return counts
+

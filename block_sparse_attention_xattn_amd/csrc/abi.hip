@@ -69,8 +69,15 @@ static xa_status_t check_tensor(const char* fn, const char* name, const void* p,
   if (tok % 8 != 0 || head % 8 != 0 || (uintptr_t)p % 16 != 0)
     return fail(XA_EINVAL, "%s: %s must be 16-byte aligned with strides that are multiples of 8 elements", fn,
                 name);
-  if (len > 1 && tok < (int64_t)heads * d && head < d)
-    return fail(XA_EINVAL, "%s: %s strides overlap rows", fn, name);
+  // rows must not alias: token-major (heads of a token side by side, tokens after them) or head-major
+  // (tokens of a head side by side, heads after them); a stride along an axis of length 1 is never used
+  const bool one_tok = len <= 1, one_head = heads <= 1;
+  bool disjoint;
+  if (one_tok && one_head) disjoint = true;
+  else if (one_tok) disjoint = head >= d;
+  else if (one_head) disjoint = tok >= d;
+  else disjoint = (head >= d && tok >= (int64_t)heads * head) || (tok >= d && head >= len * tok);
+  if (!disjoint) return fail(XA_EINVAL, "%s: %s strides overlap rows", fn, name);
   (void)dt;
   return XA_OK;
 }

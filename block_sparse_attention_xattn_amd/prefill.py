@@ -94,6 +94,14 @@ class ChunkedPrefill:
         self.seg_ws = B.workspace(B.bsa_prefill_segments_workspace_size(chunk, self.hq, self.d, 2), dev)
         self.packed = B.PackedV(self.L, self.hkv, self.d, q.dtype, dev)
         self.out = torch.empty(self.L, self.hq, self.d, dtype=self.out_dtype, device=dev)
+        # density counts (select_blocks step 5 and the comm density after step 6), accumulated over the
+        # chunks run while track_density is set: [kept causal pairs, causal pairs, kept cache blocks, cache
+        # blocks].  Chunks without the cache-block form count the cache blocks their mask would load
+        # (1024-token cache blocks, or cache_block tokens).
+        self.track_density = False
+        self.density_counts = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.density_cache_block = cache_block or 1024
+        self._keep_scratch = torch.empty(max(self.L // self.density_cache_block, 1), dtype=torch.uint8, device=dev)
         self.bufs = []
         for p in self.starts:
             c = min(chunk, self.L - p)
@@ -199,11 +207,35 @@ class ChunkedPrefill:
         c = self._len(b)
         B.attn_merge(b.o_hist, b.l_hist, b.o_cur, b.l_cur, o_out=self.out[b.p:b.p + c], lse_out=b.lse)
 
+    def record_density(self, b: ChunkBuffers):
+        """Add chunk b's compute and comm density counts to density_counts (on the stream, no host wait)."""
+        diag0 = b.p // self.block
+        if self.estimator == "downsampled":
+            diag0 = b.mask.shape[2]  # history-only mask: every column precedes the chunk
+        keep = b.keep_any
+        ncb = b.p // self.density_cache_block
+        if keep is None and ncb > 0 and self.estimator == "full":
+            keep = self._keep_scratch[:ncb]
+            B.xattn_mask_to_cache_blocks(b.mask, 0, ncb, self.density_cache_block // self.block, True,
+                                         keep_any=keep, want=("any",))
+        B.xattn_density_counts(self.density_counts, b.mask, diag0, keep if ncb > 0 else None)
+
+    def reset_density(self):
+        self.density_counts.zero_()
+
+    def density(self) -> dict:
+        """Compute and comm density of the chunks recorded since the last reset (one host read)."""
+        c = [int(x) for x in self.density_counts.cpu().tolist()]
+        return dict(selected=c[0], causal=c[1], density=c[0] / c[1] if c[1] else None,
+                    kept_cache_blocks=c[2], cache_blocks=c[3], comm_density=c[2] / c[3] if c[3] else None)
+
     def run_chunk(self, i: int):
         b = self.bufs[i]
         self.pack(b)
         self.estimate(b)
         self.reduce(b)
+        if self.track_density:
+            self.record_density(b)
         self.attend(b)
         self.merge(b)
 

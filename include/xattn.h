@@ -2,14 +2,15 @@
  * xattn.h -- C ABI of the MI355X (gfx950) XAttention block-sparse
  * chunked-prefill library (libxattn.so).
  *
- * The path has three parts plus a mask reducer:
+ * The path has three parts plus a mask reducer and the density counts:
  *   1. xattn_estimate          -- stride-S antidiagonal importance estimate and
  *                                 cumulative-threshold block selection;
  *   2. bsa_prefill             -- block-sparse flash attention over the kept
  *      (bsa_pack_v,              128-token blocks, returning out and LSE
  *       bsa_prefill_packed)      (variant reading V packed once per chunk);
  *   3. attn_merge              -- LSE merge of two partial attention results;
- *   4. xattn_mask_to_cache_blocks -- 128-token block mask -> cache blocks.
+ *   4. xattn_mask_to_cache_blocks -- 128-token block mask -> cache blocks;
+ *   5. xattn_density_counts    -- compute / comm density as integer counts.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -480,6 +481,38 @@ xa_status_t xattn_mask_to_cache_blocks(const uint8_t* block_mask, int32_t heads,
                                        int32_t force_first_last, uint8_t* keep_per_head,
                                        uint8_t* keep_any, uint8_t* keep_any_blocks,
                                        xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Density counts (compute density and comm density)
+ *
+ * XAttentionBSAPolicy.select_blocks, "Step 5: Record density": the compute
+ * density of a chunk is the number of kept (head, query block, key block)
+ * pairs on or below the causal diagonal over the number of such pairs; and
+ * the comm density recorded after step 6: the cache blocks to load over the
+ * cache blocks the history holds.  Integer counts, so a whole prefill's
+ * density is one ratio of sums (the policy's statistics accumulate the same
+ * way across chunks).
+ *   mask byte (h, qb, col) at block_mask + h*mask_head_stride + qb*mask_row_stride + col;
+ *   row qb's causal columns are 0 .. min(diag0 + qb, n_cols - 1) (diag0 = the
+ *   column of query block 0's diagonal block, q_start_pos/128 for a chunk's
+ *   mask whose column 0 is key block 0; diag0 >= n_cols - 1 counts every column,
+ *   as for a history-only mask).
+ * counts: int64_t[4] in DEVICE memory, 8-byte aligned, ADDED to (the caller
+ *   zeroes it):
+ *   counts[0] += kept causal pairs        counts[1] += causal pairs
+ *   counts[2] += nonzero keep_any bytes   counts[3] += n_cache_blocks
+ * block_mask may be NULL (counts[0..1] unchanged; heads, n_qb, n_cols, strides
+ *   ignored); keep_any may be NULL when n_cache_blocks == 0 (counts[2..3]
+ *   unchanged).  keep_any: uint8_t[n_cache_blocks], e.g. the keep_any output
+ *   of xattn_mask_to_cache_blocks.
+ * Errors: XA_EINVAL for a null or misaligned counts, heads/n_qb/n_cols <= 0 or
+ *   a negative stride with a mask, n_cache_blocks < 0, or n_cache_blocks > 0
+ *   without keep_any; nothing is launched then.
+ * ------------------------------------------------------------------------ */
+xa_status_t xattn_density_counts(const uint8_t* block_mask, int32_t heads, int32_t n_qb, int64_t n_cols,
+                                 int64_t mask_head_stride, int64_t mask_row_stride, int64_t diag0,
+                                 const uint8_t* keep_any, int64_t n_cache_blocks, int64_t* counts,
+                                 xa_stream_t stream);
 
 #ifdef __cplusplus
 }

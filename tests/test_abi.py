@@ -254,3 +254,31 @@ def test_varlen_sizes_and_rejects(lib):
     assert bsa(odt=7) == B.XA_EUNSUPPORTED
     assert bsa(d=64) == B.XA_EUNSUPPORTED
     assert bsa(wsb=need_b - 1) == B.XA_EWORKSPACE
+
+
+def test_density_counts_rejects(lib):
+    def dc(mask=FAKE, heads=4, nqb=2, ncols=16, hs=32, rs=16, diag0=14, keep=FAKE2, ncb=3, counts=FAKE):
+        return lib.xattn_density_counts(mask, heads, nqb, ncols, hs, rs, diag0, keep, ncb, counts, None)
+    assert dc(counts=None) == B.XA_EINVAL
+    assert dc(counts=ctypes.c_void_p(0x100004)) == B.XA_EINVAL        # not 8-byte aligned
+    assert dc(heads=0) == B.XA_EINVAL
+    assert dc(ncols=0) == B.XA_EINVAL
+    assert dc(rs=-16) == B.XA_EINVAL
+    assert dc(ncb=-1) == B.XA_EINVAL
+    assert dc(keep=None, ncb=3) == B.XA_EINVAL                           # cache blocks without a keep list
+    assert dc(mask=None, keep=None, ncb=0) == B.XA_OK                     # nothing to count: nothing launched
+
+
+@pytest.mark.parametrize("qt,qh,ok", [
+    (32 * 128, 128, True),          # token-major
+    (128, 4096 * 128, True),        # head-major (4096 tokens of a head, then the next head)
+    (128, 128, False),              # heads alias tokens
+    (32 * 128, 64, False),          # heads overlap inside a row
+    (64 * 128, 256, True),          # token-major with gaps (a slice of a wider buffer)
+    (128, 128 * 100, False),        # head-major but heads closer than the token extent
+])
+def test_estimate_rejects_aliasing_layouts(lib, qt, qh, ok):
+    # block_scores is null, so even an accepted layout fails validation (after the layout check): nothing launches
+    st = _estimate(lib, qt=qt, qh=qh, sc=None)
+    assert st == B.XA_EINVAL
+    assert (b"overlap" in lib.xattn_last_error()) != ok

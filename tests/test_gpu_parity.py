@@ -184,11 +184,20 @@ def test_small_multichunk_prefill_end_to_end(fused):
     out = run.run()
     torch.cuda.synchronize()
     same = True
+    qn, kn, vn = _np(q), _np(k), _np(v)
     for i, b in enumerate(run.bufs):
         PAR.check_scores(b.scores.cpu().numpy(), ref["scores"][i])
-        n_diff, _ = PAR.check_mask(b.mask.cpu().numpy(), ref["scores"][i], ref["masks"][i], b.p, 0.9)
+        n_diff, _ = PAR.check_mask(b.mask.cpu().numpy(), ref["scores"][i], ref["masks"][i], b.p, 0.9,
+                                   label=f"chunk {i}")
         same &= n_diff == 0
+        # attention is always checked: the oracle attends with the GPU's own mask (an exempt flip changes only
+        # which blocks are attended, not how), history + chunk merged by LSE
+        rows = slice(b.p, b.p + 1024)
+        ro, rl = PAR.oracle_chunk_attention(O, qn[rows], kn[:b.p + 1024], vn[:b.p + 1024], b.p, b.p,
+                                            b.mask.cpu().numpy())
+        PAR.check_out_lse(_np(out[rows]), _np(b.lse), ro, rl, PAR.OUT_ATOL_BF16)
     if same:
+        # and the oracle's whole chunked prefill (its own masks) where they agree
         PAR.check_out_lse(_np(out), np.concatenate([_np(b.lse) for b in run.bufs], axis=1), ref["out"], ref["lse"],
                           PAR.OUT_ATOL_BF16)
 
