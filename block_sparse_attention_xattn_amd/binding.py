@@ -54,6 +54,11 @@ def _declare(lib):
     lib.xattn_estimate.restype = ctypes.c_int
     lib.xattn_estimate.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
                                    I64, I32, I32, F, P, P, P, SZ, P]
+    lib.xattn_estimate_noalloc_max_bytes.restype = SZ
+    lib.xattn_estimate_noalloc_max_bytes.argtypes = []
+    lib.xattn_estimate_noalloc.restype = ctypes.c_int
+    lib.xattn_estimate_noalloc.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I64, I32, I32, I32,
+                                           I64, I32, I32, F, P, P, P]
     lib.bsa_prefill_workspace_size.restype = SZ
     lib.bsa_prefill_workspace_size.argtypes = [I64, I64, I32, I32, I32, ctypes.c_int]
     lib.bsa_prefill.restype = ctypes.c_int
@@ -272,6 +277,31 @@ def xattn_estimate(q, k, q_start_pos: int, stride: int = 8, threshold: float = 0
     _check(lib().xattn_estimate(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), dt,
                                 q_len, k_len, hq, hkv, d, q_start_pos, stride, block, float(threshold),
                                 _ptr(block_scores), _ptr(block_mask), _ptr(ws), ws.numel(), _stream(stream)))
+    return block_scores, block_mask
+
+
+def xattn_estimate_noalloc(q, k, q_start_pos: int, stride: int = 8, threshold: float = 0.9, block: int = 128,
+                           block_scores=None, block_mask=None, stream=None):
+    """xattn_estimate with the library's own working memory (no workspace; see xattn.h).  Returns (scores, mask);
+    pass preallocated block_scores / block_mask to allocate nothing here either."""
+    _qkv_check(q, "q")
+    _qkv_check(k, "k")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype:
+        raise XattnError(XA_EINVAL, "q and k dtypes differ")
+    q_len, hq, d = q.shape
+    k_len, hkv, _ = k.shape
+    n_qb, nkb = q_len // block, k_len // block
+    if block_scores is None:
+        block_scores = torch.empty(hq, n_qb, nkb, dtype=torch.float32, device=q.device)
+    if block_mask is None:
+        block_mask = torch.empty(hq, n_qb, nkb, dtype=torch.uint8, device=q.device)
+    _dense_check(block_scores, "block_scores", (hq, n_qb, nkb), torch.float32, q.device)
+    _dense_check(block_mask, "block_mask", (hq, n_qb, nkb), block_mask.dtype if block_mask.dtype == torch.bool
+                 else torch.uint8, q.device)
+    _check(lib().xattn_estimate_noalloc(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), dt,
+                                        q_len, k_len, hq, hkv, d, q_start_pos, stride, block, float(threshold),
+                                        _ptr(block_scores), _ptr(block_mask), _stream(stream)))
     return block_scores, block_mask
 
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <vector>
 
 #include "launchers.h"
@@ -204,12 +205,12 @@ xa_status_t estimate_core(const char* fn, const void* q, int64_t q_tok, int64_t 
 }
 }  // namespace
 
-extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
-                                      int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len,
-                                      int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int32_t stride,
-                                      int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
-                                      void* workspace, size_t ws_bytes, xa_stream_t stream) {
-  const char* fn = "xattn_estimate";
+namespace {
+// Argument checks of xattn_estimate (everything but the workspace); fills the workspace layout.
+xa_status_t validate_estimate(const char* fn, const void* q, int64_t q_tok, int64_t q_head, const void* k,
+                              int64_t k_tok, int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len,
+                              int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int32_t stride, int32_t block,
+                              float threshold, float* block_scores, uint8_t* block_mask, EstLayout& L) {
   xa_status_t st;
   if ((st = check_heads(fn, hq, hkv, d)) != XA_OK) return st;
   if (dtype != XA_F32 && dtype != XA_BF16) return fail(XA_EUNSUPPORTED, "%s: dtype must be XA_F32 or XA_BF16", fn);
@@ -224,15 +225,93 @@ extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_he
   if ((st = check_tensor(fn, "q", q, q_tok, q_head, q_len, hq, d, dtype)) != XA_OK) return st;
   if ((st = check_tensor(fn, "k", k, k_tok, k_head, k_len, hkv, d, dtype)) != XA_OK) return st;
   if (!block_scores || !block_mask) return fail(XA_EINVAL, "%s: block_scores and block_mask are required", fn);
-  const EstLayout L = est_layout(q_len, k_len, hq, hkv, d, stride, block, dtype);
+  const int64_t R = q_len / stride, nkb = k_len / block;
+  if ((int64_t)hq * nkb * R > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
+  L = est_layout(q_len, k_len, hq, hkv, d, stride, block, dtype);
+  return XA_OK;
+}
+}  // namespace
+
+extern "C" xa_status_t xattn_estimate(const void* q, int64_t q_tok, int64_t q_head, const void* k, int64_t k_tok,
+                                      int64_t k_head, xa_dtype_t dtype, int64_t q_len, int64_t k_len,
+                                      int32_t hq, int32_t hkv, int32_t d, int64_t q_start, int32_t stride,
+                                      int32_t block, float threshold, float* block_scores, uint8_t* block_mask,
+                                      void* workspace, size_t ws_bytes, xa_stream_t stream) {
+  const char* fn = "xattn_estimate";
+  EstLayout L{};
+  xa_status_t st = validate_estimate(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, k_len, hq, hkv, d,
+                                     q_start, stride, block, threshold, block_scores, block_mask, L);
+  if (st != XA_OK) return st;
   if (!workspace || ws_bytes < L.total || (uintptr_t)workspace % 256 != 0)
     return fail(XA_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, L.total,
                 ws_bytes);
-  const int64_t R = q_len / stride, nkb = k_len / block;
-  if ((int64_t)hq * nkb * R > ((int64_t)1 << 40)) return fail(XA_EUNSUPPORTED, "%s: problem too large", fn);
   return estimate_core(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, k_len, hq, hkv, d, stride,
                        block / stride, q_start, q_len / block, q_start / block, false, threshold, block_scores,
                        block_mask, static_cast<char*>(workspace), L, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// xattn_estimate_noalloc: xattn_estimate with its working memory (the per-(row, key block) log-sum-exp
+// partials, plus the bf16 hi / lo planes of fp32 inputs) in `scratch`, a device array of the library, so the
+// caller passes no workspace and nothing is allocated.  Each device holds its own copy of the array; its
+// address on a device comes from hipGetSymbolAddress, taken once per device (with that device current) and
+// kept.  The array's name in host code is only a host-side handle: kernels get the kept device address.
+// Nothing in the array has to start at zero (the GEMM writes every partial the selection reads), so calls
+// clear nothing; calls that overlap on one device share the array and race.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices];  // device address of `scratch` on device i (null until first use)
+
+xa_status_t device_scratch(const char* fn, hipStream_t s, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(XA_EHIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(XA_EUNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  if (s != nullptr) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return fail(XA_EHIP, "%s: hipStreamGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (sd != dev)
+      return fail(XA_EINVAL, "%s: the stream belongs to device %d but device %d is current", fn, (int)sd, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(XA_EHIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return XA_OK;
+}
+}  // namespace
+
+extern "C" size_t xattn_estimate_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" xa_status_t xattn_estimate_noalloc(const void* q, int64_t q_tok, int64_t q_head, const void* k,
+                                              int64_t k_tok, int64_t k_head, xa_dtype_t dtype, int64_t q_len,
+                                              int64_t k_len, int32_t hq, int32_t hkv, int32_t d, int64_t q_start,
+                                              int32_t stride, int32_t block, float threshold, float* block_scores,
+                                              uint8_t* block_mask, xa_stream_t stream) {
+  const char* fn = "xattn_estimate_noalloc";
+  EstLayout L{};
+  xa_status_t st = validate_estimate(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, k_len, hq, hkv, d,
+                                     q_start, stride, block, threshold, block_scores, block_mask, L);
+  if (st != XA_OK) return st;
+  if (L.total > kScratchBytes)
+    return fail(XA_EUNSUPPORTED, "%s: needs %zu bytes of working memory, the library's array holds %zu", fn,
+                L.total, kScratchBytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  if ((st = device_scratch(fn, s, &ws)) != XA_OK) return st;
+  return estimate_core(fn, q, q_tok, q_head, k, k_tok, k_head, dtype, q_len, k_len, hq, hkv, d, stride,
+                       block / stride, q_start, q_len / block, q_start / block, false, threshold, block_scores,
+                       block_mask, ws, L, s);
 }
 
 // ---------------------------------------------------------------------------

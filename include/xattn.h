@@ -123,6 +123,30 @@ xa_status_t xattn_estimate(const void* q, int64_t q_tok_stride, int64_t q_head_s
                            void* workspace, size_t workspace_bytes, xa_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * xattn_estimate without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs, kernels and
+ * results as xattn_estimate, except that the working memory lives in a
+ * device array inside the library (xattn_estimate_noalloc_max_bytes() bytes,
+ * 64 MiB: enough for 32 query heads against 131072 keys at stride 8 with
+ * bf16 inputs), one copy per GPU, held until the process ends.  The call
+ * allocates and frees nothing.  Requirements as for xattn_estimate, plus:
+ * the working memory xattn_estimate_workspace_size(...) would ask for must
+ * not exceed that maximum (else XA_EUNSUPPORTED, nothing launched), and
+ * `stream` must belong to the current device (else XA_EINVAL).  The array
+ * needs no clearing between calls; calls that overlap on one GPU (several
+ * streams or host threads at once) share it and race: order them.
+ * ------------------------------------------------------------------------ */
+size_t xattn_estimate_noalloc_max_bytes(void);
+
+xa_status_t xattn_estimate_noalloc(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                   const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                                   xa_dtype_t dtype, int64_t q_len, int64_t k_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int64_t q_start_pos, int32_t stride, int32_t block, float threshold,
+                                   float* block_scores, uint8_t* block_mask, xa_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Part 2: block-sparse flash attention with LSE  (block_sparse_attn_func /
  * flash_attn_with_lse on the pages)
  *
