@@ -28,6 +28,7 @@
 //   * the walk over key blocks touches only kept blocks, in ascending order,
 //     from a list built in LDS from the mask row.
 // XA_F32 inputs use bf16 hi/lo planes and three MFMAs per product.
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -511,6 +512,9 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
   const bf16* vg = P.vt_hi + (int64_t)kvh * P.vt_head;
   char* kt = smem + grp * (KTB + VTB);
   char* vt = kt + KTB;
+  // loop-invariant arguments in registers (the tick loop would otherwise reload them from the kernel arguments)
+  const int64_t kv_len = P.kv_len, kv_start = P.kv_start, k_tok = P.k_tok, vt_pitch = P.vt_pitch;
+  const bool causal = P.causal != 0;
 
   // Piece i of this wave's share of a K (V^T) tile covers rows r = 32 wave + 4 i + lane / 16 (16 lanes of
   // 16 bytes per 256-byte row), lane chunk (lane % 16) ^ (r % 16).  r % 16 = 4 (i % 4) + lane / 16, so the
@@ -521,22 +525,29 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 32 + (lane >> 4);
     const int ch = (lane & 15) ^ (4 * j + (lane >> 4));
-    kx[j] = (uint32_t)(((int64_t)r * P.k_tok + ch * 8) * 2);
-    vx[j] = (uint32_t)(((int64_t)r * P.vt_pitch + ch * 8) * 2);
+    kx[j] = (uint32_t)(((int64_t)r * k_tok + ch * 8) * 2);
+    vx[j] = (uint32_t)(((int64_t)r * vt_pitch + ch * 8) * 2);
   }
-  const uint32_t kstep = (uint32_t)(8 * P.k_tok);     // 4 rows of K, bytes
-  const uint32_t vstep = (uint32_t)(8 * P.vt_pitch);  // 4 rows of V^T, bytes
+  const uint32_t kstep = (uint32_t)(8 * k_tok);     // 4 rows of K, bytes
+  const uint32_t vstep = (uint32_t)(8 * vt_pitch);  // 4 rows of V^T, bytes
+  // The LDS destination of piece i is this wave's first piece + i KiB.  The first piece's offset goes through an
+  // empty asm at every call, so the compiler derives the eight destinations from one register each time instead
+  // of keeping all sixteen (K and V) in scalar registers across the loop.
   auto issue_k = [&](int jb) {
     const int64_t j0 = (int64_t)jb * kBlk;
-    const int64_t rows = P.kv_len - j0 < kBlk ? P.kv_len - j0 : kBlk;
-    const auto rs = tile_rsrc(kg + j0 * P.k_tok, (uint32_t)(((rows - 1) * P.k_tok + D) * 2));
+    const int64_t rows = kv_len - j0 < kBlk ? kv_len - j0 : kBlk;
+    const auto rs = tile_rsrc(kg + j0 * k_tok, (uint32_t)(((rows - 1) * k_tok + D) * 2));
+    uint32_t d0 = (uint32_t)(wave * KI * 1024);
+    asm volatile("" : "+s"(d0));
 #pragma unroll
-    for (int i = 0; i < KI; ++i) buf2lds16(rs, kx[i & 3] + i * kstep, kt + (wave * KI + i) * 1024);
+    for (int i = 0; i < KI; ++i) buf2lds16(rs, kx[i & 3] + i * kstep, kt + d0 + i * 1024);
   };
   auto issue_v = [&](int jb) {
-    const auto rs = tile_rsrc(vg + (int64_t)jb * kBlk, (uint32_t)(((int64_t)(D - 1) * P.vt_pitch + kBlk) * 2));
+    const auto rs = tile_rsrc(vg + (int64_t)jb * kBlk, (uint32_t)(((int64_t)(D - 1) * vt_pitch + kBlk) * 2));
+    uint32_t d0 = (uint32_t)(wave * VI * 1024);
+    asm volatile("" : "+s"(d0));
 #pragma unroll
-    for (int i = 0; i < VI; ++i) buf2lds16(rs, vx[i & 3] + i * vstep, vt + (wave * VI + i) * 1024);
+    for (int i = 0; i < VI; ++i) buf2lds16(rs, vx[i & 3] + i * vstep, vt + d0 + i * 1024);
   };
 
   f32x16 sacc[4];
@@ -545,25 +556,29 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
     {
       // each of the eight waves scans an eighth of the segment: count, exchange, write
+      // a wave's share is at most two rounds of 64 columns: both rounds' bytes are read at once and their
+      // ballots kept, so the mask row is read once
+      static_assert(kListMax / 8 <= 128, "at most two 64-column rounds per wave");
       const int64_t part8 = ((seg_end - seg + 7) / 8 + 63) / 64 * 64;
       const int64_t w0 = seg + wave8 * part8;
       const int64_t w1 = w0 + part8 < seg_end ? w0 + part8 : seg_end;
-      int mine = 0;
-      for (int64_t base = w0; base < w1; base += 64) {
-        const int64_t jb = base + lane;
-        mine += __popcll(__ballot(jb < w1 && (mrow == nullptr || mrow[jb] != 0)));
+      bool hit[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int64_t jb = w0 + 64 * t + lane;
+        hit[t] = jb < w1 && (mrow == nullptr || mrow[jb] != 0);
       }
-      if (lane == 0) s_wcnt[wave8] = mine;
+      const uint64_t bal0 = __ballot(hit[0]);
+      const uint64_t bal1 = __ballot(hit[1]);
+      if (lane == 0) s_wcnt[wave8] = __popcll(bal0) + __popcll(bal1);
       __syncthreads();
       int pos0 = 0;
       for (int w = 0; w < wave8; ++w) pos0 += s_wcnt[w];
-      for (int64_t base = w0; base < w1; base += 64) {
-        const int64_t jb = base + lane;
-        const bool keep = jb < w1 && (mrow == nullptr || mrow[jb] != 0);
-        const uint64_t bal = __ballot(keep);
-        if (keep) s_list[pos0 + __popcll(bal & ((1ull << lane) - 1))] = (int)jb;
-        pos0 += __popcll(bal);
-      }
+      const uint64_t below = (1ull << lane) - 1;
+      if (hit[0]) s_list[pos0 + __popcll(bal0 & below)] = (int)(w0 + lane);
+      pos0 += __popcll(bal0);
+      if (hit[1]) s_list[pos0 + __popcll(bal1 & below)] = (int)(w0 + 64 + lane);
+      pos0 += __popcll(bal1);
       if (wave8 == 7 && lane == 0) s_cnt = pos0;
     }
     __syncthreads();
@@ -613,10 +628,10 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
         const int jb = __builtin_amdgcn_readfirstlane(s_list[grp + 2 * i]);
         issue_v(jb);
         const int64_t key0 = (int64_t)jb * kBlk;
-        if ((key0 + kBlk > P.kv_len) || (P.causal && P.kv_start + key0 + kBlk - 1 > wave_q_lo)) {
-          int64_t lim = P.kv_len - 1 - key0;
-          const int64_t qlim = wave_q_lo - P.kv_start - key0 + n;  // causal limit of this lane's row
-          if (P.causal && qlim < lim) lim = qlim;
+        if ((key0 + kBlk > kv_len) || (causal && kv_start + key0 + kBlk - 1 > wave_q_lo)) {
+          int64_t lim = kv_len - 1 - key0;
+          const int64_t qlim = wave_q_lo - kv_start - key0 + n;  // causal limit of this lane's row
+          if (causal && qlim < lim) lim = qlim;
           const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
@@ -791,6 +806,333 @@ __global__ __launch_bounds__(512, 1) void bsa3_kernel(BsaMulti M) {
 }
 
 // ---------------------------------------------------------------------------
+// Pair form (bf16, head_dim 128, an even number of query heads per kv head):
+// one workgroup of eight waves per CU computes two query heads of one kv head
+// for one 128-row query block.  The query heads of a kv head keep nearly the
+// same key blocks, so each K / V^T tile is brought into LDS once for both:
+// group g (waves 4g .. 4g+3, 32 rows each) computes head 2p + g over the union
+// of the two heads' kept lists, skipping (no MFMA, no softmax) the blocks its
+// own head did not keep, so each head's result is exactly its own.  The groups
+// stay one phase apart as in the ping-pong form (group 0's matrix phase of
+// block i meets group 1's vector phase of block i-1), and the tiles are double
+// buffered: K of block i in K slot i % 2, V^T of block i in V slot i % 2.
+// Group 1 brings K of block i + 2 during its vector phase of block i (two
+// phases before group 0 needs it; it waits at the end of its next matrix
+// phase), group 0 brings V^T of block i during its vector phase of block i (one
+// phase before its P V^T of block i), so each wave issues eight 1 KiB tile
+// pieces per vector phase instead of sixteen.
+// ---------------------------------------------------------------------------
+template <int D, typename OutT>
+__device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid) {
+  static_assert(D == 128, "pair form: head_dim 128");
+  constexpr int KCH = D / 8;
+  constexpr int KTB = 128 * KCH * 16;     // K tile bytes
+  constexpr int VTB = D * 256;            // V^T tile bytes
+  constexpr int NKK = D / 16;
+  constexpr int NMD = D / 32;
+  constexpr int KI = KCH / 2;
+  constexpr int VI = D / 16;
+  constexpr float kRescale = 8.0f;
+  constexpr int kOwnShift = 29;           // list entry: key block | (kept by head 2p) << 29 | (by 2p + 1) << 30
+  constexpr int kBlockBits = (1 << kOwnShift) - 1;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (KTB + VTB)];  // K slots 0, 1, then V^T slots 0, 1
+  __shared__ int s_list[kListMax];
+  __shared__ int s_cnt;
+  __shared__ int s_wcnt[8];
+
+  const int wave8 = wave_id();
+  const int grp = wave8 >> 2;
+  const int wave = wave8 & 3;
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  int hp, qb;
+  bsa_decode(bid, P.group / 2, P.hkv, P.n_qb, hp, qb);
+  const int h = 2 * hp + grp;  // this group's query head
+  const int kvh = h / P.group;
+  const int64_t row0 = (int64_t)qb * kBlk + wave * 32;
+  const int64_t wave_q_lo = P.q_start + row0;
+  const float c = P.scale_log2;
+
+  bf16x8 qf[NKK];
+  {
+    const int64_t off = (row0 + n) * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q_hi + off + kk * 16));
+  }
+  f32x16 o[NMD];
+#pragma unroll
+  for (int i = 0; i < NMD; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
+  const int64_t gb0 = P.kv_start / kBlk;
+  int64_t jb_end = nkb;
+  if (P.causal) {
+    const int64_t lim = P.q_start + (int64_t)qb * kBlk + (kBlk - 1) - P.kv_start;
+    jb_end = lim < 0 ? 0 : (lim / kBlk + 1 < nkb ? lim / kBlk + 1 : nkb);
+  }
+  int64_t jb_lo = 0;
+  if (part == 1) jb_end = M.mid[item];
+  if (part == 2) jb_lo = M.mid[item];
+  const uint8_t* mrow0 =
+      P.mask ? P.mask + (int64_t)(2 * hp) * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
+  const uint8_t* mrow1 = P.mask ? mrow0 + P.mask_hs : nullptr;
+  const bf16* kg = P.k_hi + (int64_t)kvh * P.k_head;
+  const bf16* vg = P.vt_hi + (int64_t)kvh * P.vt_head;
+  const int64_t kv_len = P.kv_len, kv_start = P.kv_start, k_tok = P.k_tok, vt_pitch = P.vt_pitch;
+  const bool causal = P.causal != 0;
+  const int own_bit = 1 << (kOwnShift + grp);
+
+  // Piece i of this wave's share of a tile covers rows r = 32 wave + 4 i + lane / 16, lane chunk
+  // (lane % 16) ^ (r % 16): byte offset kx[i % 4] + i * 4 rows (as in the ping-pong form).
+  static_assert(KCH == 16 && KI == 8 && VI == 8, "tile pieces: 16 chunks per row, 8 pieces per wave");
+  uint32_t kx[4], vx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + (lane >> 4);
+    const int ch = (lane & 15) ^ (4 * j + (lane >> 4));
+    kx[j] = (uint32_t)(((int64_t)r * k_tok + ch * 8) * 2);
+    vx[j] = (uint32_t)(((int64_t)r * vt_pitch + ch * 8) * 2);
+  }
+  const uint32_t kstep = (uint32_t)(8 * k_tok);
+  const uint32_t vstep = (uint32_t)(8 * vt_pitch);
+  // K of block jb into K slot sl; the four waves of the calling group bring the whole tile
+  auto issue_k = [&](int jb, int sl) {
+    const int64_t j0 = (int64_t)jb * kBlk;
+    const int64_t rows = kv_len - j0 < kBlk ? kv_len - j0 : kBlk;
+    const auto rs = tile_rsrc(kg + j0 * k_tok, (uint32_t)(((rows - 1) * k_tok + D) * 2));
+    uint32_t d0 = (uint32_t)(sl * KTB + wave * KI * 1024);
+    asm volatile("" : "+s"(d0));
+#pragma unroll
+    for (int i = 0; i < KI; ++i) buf2lds16(rs, kx[i & 3] + i * kstep, smem + d0 + i * 1024);
+  };
+  auto issue_v = [&](int jb, int sl) {
+    const auto rs = tile_rsrc(vg + (int64_t)jb * kBlk, (uint32_t)(((int64_t)(D - 1) * vt_pitch + kBlk) * 2));
+    uint32_t d0 = (uint32_t)(2 * KTB + sl * VTB + wave * VI * 1024);
+    asm volatile("" : "+s"(d0));
+#pragma unroll
+    for (int i = 0; i < VI; ++i) buf2lds16(rs, vx[i & 3] + i * vstep, smem + d0 + i * 1024);
+  };
+  auto entry = [&](int i) { return __builtin_amdgcn_readfirstlane(s_list[i]); };
+
+  f32x16 sacc[4];
+  bf16x8 pf[8];
+  for (int64_t seg = jb_lo; seg < jb_end; seg += kListMax) {
+    const int64_t seg_end = seg + kListMax < jb_end ? seg + kListMax : jb_end;
+    {
+      // union list of the two heads' kept blocks, each entry tagged with the heads that kept it: each of the
+      // eight waves reads at most two rounds of 64 columns of both mask rows at once
+      static_assert(kListMax / 8 <= 128, "at most two 64-column rounds per wave");
+      const int64_t part8 = ((seg_end - seg + 7) / 8 + 63) / 64 * 64;
+      const int64_t w0 = seg + wave8 * part8;
+      const int64_t w1 = w0 + part8 < seg_end ? w0 + part8 : seg_end;
+      int tag[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int64_t jb = w0 + 64 * t + lane;
+        const bool in = jb < w1;
+        const bool a = in && (mrow0 == nullptr || mrow0[jb] != 0);
+        const bool b = in && (mrow1 == nullptr || mrow1[jb] != 0);
+        tag[t] = (a ? 1 << kOwnShift : 0) | (b ? 2 << kOwnShift : 0);
+      }
+      const uint64_t bal0 = __ballot(tag[0] != 0);
+      const uint64_t bal1 = __ballot(tag[1] != 0);
+      if (lane == 0) s_wcnt[wave8] = __popcll(bal0) + __popcll(bal1);
+      __syncthreads();
+      int pos0 = 0;
+      for (int w = 0; w < wave8; ++w) pos0 += s_wcnt[w];
+      const uint64_t below = (1ull << lane) - 1;
+      if (tag[0]) s_list[pos0 + __popcll(bal0 & below)] = (int)(w0 + lane) | tag[0];
+      pos0 += __popcll(bal0);
+      if (tag[1]) s_list[pos0 + __popcll(bal1 & below)] = (int)(w0 + 64 + lane) | tag[1];
+      pos0 += __popcll(bal1);
+      if (wave8 == 7 && lane == 0) s_cnt = pos0;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    const int iters = cnt == 0 ? 0 : cnt + 1;
+    // K of the first two blocks: group 0 the first, group 1 the second
+    if (grp < cnt) issue_k(entry(grp) & kBlockBits, grp);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    __syncthreads();
+    static_assert(NMD == 4, "fragment ring: four output / score tiles");
+    // matrix phase i: P V^T of block i-1 (V slot (i-1) % 2), then K Q^T of block i (K slot i % 2), each only if
+    // this group's head kept the block
+    auto mphase = [&](int i) {
+      bf16x8 fr[4];
+      if (i >= 1 && (entry(i - 1) & own_bit)) {
+        const char* vt = smem + 2 * KTB + ((i - 1) & 1) * VTB;
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) fr[md] = lds_frag<128>(vt, md * 32 + n, hh);
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2)
+#pragma unroll
+          for (int md = 0; md < NMD; ++md) {
+            o[md] = mfma32(fr[md], pf[k2], o[md]);
+            if (k2 + 1 < 8) fr[md] = lds_frag<128>(vt, md * 32 + n, 2 * (k2 + 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (i < cnt && (entry(i) & own_bit)) {
+        const char* kt = smem + (i & 1) * KTB;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fr[mt] = lds_frag<D>(kt, mt * 32 + n, hh);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            sacc[mt] = mfma32(fr[mt], qf[kk], sacc[mt]);
+            if (kk + 1 < NKK) fr[mt] = lds_frag<D>(kt, mt * 32 + n, 2 * (kk + 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+    };
+    // vector phase i: group 0 brings V^T of block i, group 1 K of block i + 2; then the softmax of block i
+    auto vphase = [&](int i) {
+      if (grp == 0 && i < cnt) issue_v(entry(i) & kBlockBits, i & 1);
+      if (grp == 1 && i + 2 < cnt) issue_k(entry(i + 2) & kBlockBits, i & 1);
+      if (i < cnt) {
+        const int e = entry(i);
+        if (e & own_bit) {
+          const int64_t key0 = (int64_t)(e & kBlockBits) * kBlk;
+          if ((key0 + kBlk > kv_len) || (causal && kv_start + key0 + kBlk - 1 > wave_q_lo)) {
+            int64_t lim = kv_len - 1 - key0;
+            const int64_t qlim = wave_q_lo - kv_start - key0 + n;
+            if (causal && qlim < lim) lim = qlim;
+            const int lim32 = (int)(lim < -1 ? -1 : (lim > kBlk ? kBlk : lim)) - 4 * hh;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int q = 0; q < 16; ++q) {
+                const int kl = mt * 32 + 8 * (q / 4) + (q % 4);
+                sacc[mt][q] = kl <= lim32 ? sacc[mt][q] : -INFINITY;
+              }
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sacc[mt][q]);
+          mx = halves_max(mx);
+          const bool upd = mx > m_run && (m_run == -INFINITY || (mx - m_run) * c > kRescale);
+          if (__builtin_amdgcn_ballot_w64(upd)) {
+            const float m_new = upd ? mx : m_run;
+            const float alpha = upd ? fast_exp2((m_run - m_new) * c) : 1.f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int md = 0; md < NMD; ++md) o[md] *= alpha;
+          }
+          const float mref = m_run == -INFINITY ? 0.f : m_run * c;
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p = fast_exp2(__builtin_fmaf(sacc[k2 >> 1][8 * (k2 & 1) + j], c, -mref));
+              l_run += p;
+              pf[k2][j] = (bf16)p;
+            }
+        }
+      }
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): V^T of block i landed
+    };
+    // group 1 starts one barrier later (its matrix phase i meets group 0's vector phase i) and group 0 passes
+    // one more barrier at the end; group 1 waits for its K loads at the end of each matrix phase
+    if (grp == 1) __syncthreads();
+    for (int i = 0; i < iters; ++i) {
+      mphase(i);
+      if (grp == 1) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): K of block i + 1 landed
+      __syncthreads();
+      vphase(i);
+      __syncthreads();
+    }
+    if (grp == 0) __syncthreads();
+  }
+
+  // each group finalises its own head
+  const float l_row = halves_sum(l_run);
+  float inv = 0.f, lse_v = -INFINITY;
+  if (l_row > 0.f) {
+    inv = 1.f / l_row;
+    lse_v = (m_run * c + log2f(l_row)) * kLn2;
+  }
+  if (part != 0) {
+    const size_t ps = ((size_t)(2 * M.slot[item] + part - 1) * 2 + grp) * kBlk + wave * 32 + n;
+    float* po = M.part_o + ps * D;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hh;
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[md][g4 * 4] * inv, o[md][g4 * 4 + 1] * inv,
+                                                   o[md][g4 * 4 + 2] * inv, o[md][g4 * 4 + 3] * inv};
+      }
+    if (hh == 0) M.part_lse[ps] = lse_v;
+    return;
+  }
+  if (hh == 0) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
+  OutT* out = reinterpret_cast<OutT*>(P.out);
+  if constexpr (sizeof(OutT) == 2) {
+    // both heads' rows through LDS (the tile slots are free: every wave passed the loop's last barrier and
+    // no tile load is outstanding), then all eight waves write whole 256-byte rows
+    constexpr int kStgPitch = D * 2 + 16;
+    static_assert(2 * 128 * kStgPitch <= 2 * (KTB + VTB), "staging fits the tile slots");
+    __syncthreads();
+    char* stg = smem + grp * 128 * kStgPitch;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hh;
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (bf16)(o[md][g4 * 4 + e] * inv);
+        *reinterpret_cast<u32x2*>(stg + (wave * 32 + n) * kStgPitch + d0 * 2) = __builtin_bit_cast(u32x2, pk);
+      }
+    __syncthreads();
+    // 2 heads x 128 rows x 16 pieces of 16 bytes over 512 lanes: lanes 16 j .. 16 j + 15 write one row
+    const int64_t rbase = (int64_t)qb * kBlk;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = j * 512 + (int)threadIdx.x;
+      const int g = q >> 11, r = (q >> 4) & 127, ch = q & 15;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(smem + (g * 128 + r) * kStgPitch + ch * 16);
+      *reinterpret_cast<u32x4*>(out + (rbase + r) * ((int64_t)P.hq * D) + (int64_t)(2 * hp + g) * D + ch * 8) = val;
+    }
+  } else {
+    const int64_t obase = (row0 + n) * ((int64_t)P.hq * D) + (int64_t)h * D;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hh;
+        *reinterpret_cast<f32x4*>(out + obase + d0) = f32x4{o[md][g4 * 4] * inv, o[md][g4 * 4 + 1] * inv,
+                                                            o[md][g4 * 4 + 2] * inv, o[md][g4 * 4 + 3] * inv};
+      }
+  }
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(512, 1) void bsa_pair_kernel(BsaMulti M) {
+  __shared__ int s_item;
+  const int n_items = M.n_items;
+  if ((int)blockIdx.x >= n_items && (int)blockIdx.x >= n_items + M.ctl[2]) return;
+  if (threadIdx.x == 0) s_item = take_entry(M);
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_item);
+  if (e < 0) return;
+  const int item = e >> 2, part = e & 3;
+  int item0;
+  const BsaParams& P = find_seg(M, item, item0);
+  bsa_pair_body<D, OutT>(M, P, item, part, item - item0);
+}
+
+// ---------------------------------------------------------------------------
 // Workspace preparation
 // ---------------------------------------------------------------------------
 
@@ -906,7 +1248,12 @@ __device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int&
   BsaParams P;
   if constexpr (VARLEN) P = varlen_params<D, OutT>(M, item, item0);
   else P = find_seg(M, item, item0);
-  bsa_decode(item - item0, P.group, P.hkv, P.n_qb, h, qb);
+  if (M.pair) {
+    bsa_decode(item - item0, P.group / 2, P.hkv, P.n_qb, h, qb);
+    h *= 2;  // the pair's first query head
+  } else {
+    bsa_decode(item - item0, P.group, P.hkv, P.n_qb, h, qb);
+  }
   const int64_t nkb = (P.kv_len + kBlk - 1) / kBlk;
   jb_end = nkb;
   if (P.causal) {
@@ -918,6 +1265,7 @@ __device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int&
 
 // One wave per work item: kept key blocks below the causal limit, and the key
 // block of its (count / 2)-th kept block (0-based), where a second half starts.
+// A pair item counts the blocks either of its two heads kept.
 template <bool VARLEN>
 __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items, int* __restrict__ weights,
                                                          int* __restrict__ mid) {
@@ -934,8 +1282,10 @@ __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items
     half_at = jb_end / 2;
   } else {
     const uint8_t* mrow = P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (P.kv_start / kBlk - P.mask_off);
+    const int64_t other = M.pair ? P.mask_hs : 0;  // the pair's second head (itself for single-head items)
+    auto kept_at = [&](int64_t jb) { return (mrow[jb] | mrow[jb + other]) != 0; };
     cnt = 0;
-    for (int64_t jb = lane; jb < jb_end; jb += 64) cnt += mrow[jb] != 0;
+    for (int64_t jb = lane; jb < jb_end; jb += 64) cnt += kept_at(jb);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
     const int target = cnt / 2;
@@ -943,7 +1293,7 @@ __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items
     int run = 0;
     for (int64_t base = 0; base < jb_end; base += 64) {
       const int64_t jb = base + lane;
-      const bool kept = jb < jb_end && mrow[jb] != 0;
+      const bool kept = jb < jb_end && kept_at(jb);
       const uint64_t bal = __ballot(kept);
       const int c = __popcll(bal);
       if (run + c > target) {
@@ -1071,15 +1421,17 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
 // LSE merge of the two halves of split item k (partial slot k) into its
 // segment's out and lse (both -inf: out 0, lse -inf).
 template <int D, typename OutT, bool VARLEN>
-__device__ void split_merge_one(const BsaMulti& M, int k) {
+__device__ void split_merge_one(const BsaMulti& M, int k, int e_head) {
   const int item = M.split_items[k];
   int h, qb;
   int64_t jb_end;
   const BsaParams P = item_span<D, OutT, VARLEN>(M, item, h, qb, jb_end);
-  const float* la = M.part_lse + (size_t)(2 * k) * kBlk;
-  const float* lb = la + kBlk;
-  const float* oa = M.part_o + (size_t)(2 * k) * kBlk * D;
-  const float* ob = oa + (size_t)kBlk * D;
+  const int nh = M.pair ? 2 : 1;  // heads per item; partial (slot k, half p, head e) at ((2 k + p) nh + e) rows
+  h += e_head;
+  const float* la = M.part_lse + ((size_t)(2 * k) * nh + e_head) * kBlk;
+  const float* lb = la + (size_t)nh * kBlk;
+  const float* oa = M.part_o + ((size_t)(2 * k) * nh + e_head) * kBlk * D;
+  const float* ob = oa + (size_t)nh * kBlk * D;
   OutT* out = reinterpret_cast<OutT*>(P.out);
   for (int e = (int)threadIdx.x; e < kBlk * (D / 4); e += 256) {
     const int r = e / (D / 4);
@@ -1115,7 +1467,9 @@ __device__ void split_merge_one(const BsaMulti& M, int k) {
 // Split halves are merged by a small grid that strides over the slots in use.
 template <int D, typename OutT, bool VARLEN>
 __global__ __launch_bounds__(256) void split_merge_kernel(BsaMulti M) {
-  for (int k = (int)blockIdx.x; k < M.ctl[2]; k += (int)gridDim.x) split_merge_one<D, OutT, VARLEN>(M, k);
+  const int nh = M.pair ? 2 : 1;
+  for (int k = (int)blockIdx.x; k < M.ctl[2] * nh; k += (int)gridDim.x)
+    split_merge_one<D, OutT, VARLEN>(M, k / nh, k % nh);
 }
 
 // One attention workgroup (eight waves, 132 KiB of LDS) per compute unit.
@@ -1152,6 +1506,16 @@ static bool tile_offsets_fit(const BsaParams* segs, int n_seg, int D) {
   return true;
 }
 
+// The pair form is used wherever it applies; XATTN_PAIR=0 in the environment keeps the single-head form (for
+// comparisons), read once per process.
+static bool pair_form_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("XATTN_PAIR");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 static thread_local hipEvent_t t_attn_events[2] = {nullptr, nullptr};
 void set_attention_events(hipEvent_t before, hipEvent_t after) {
   t_attn_events[0] = before;
@@ -1166,21 +1530,29 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
   if constexpr (!SPLIT && D == 128) {
     if (tile_offsets_fit(segs, n_seg, D)) {
       BsaMulti m{};
+      // pair items (two query heads of one kv head per workgroup) when every segment has an even number of
+      // query heads per kv head and a work order is available; the plan's arrays, sized for single-head
+      // items, hold half as many pair items with two heads per split slot
+      bool pair = plan != nullptr && pair_form_enabled();
+      for (int i = 0; i < n_seg; ++i) pair = pair && segs[i].group % 2 == 0;
+      m.pair = pair ? 1 : 0;
       int total = 0;
       for (int i = 0; i < n_seg; ++i) {
         m.seg[i] = segs[i];
-        total += segs[i].hq * segs[i].n_qb;
+        total += (pair ? segs[i].hq / 2 : segs[i].hq) * segs[i].n_qb;
         m.wg_end[i] = total;
       }
       m.n_seg = n_seg;
       m.n_items = total;
       if (total > 0) {
         int grid = total;
+        int max_split = 0;
         if (plan) {
+          max_split = pair ? plan->max_split / 2 : plan->max_split;
           hipLaunchKernelGGL(plan_count_kernel<false>, dim3((total + 3) / 4), dim3(256), 0, s, m, total,
                              plan->weights, plan->mid);
           hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, total, (const int*)plan->weights,
-                             plan->order, plan->ctl, plan->slot, plan->split_items, plan->max_split, plan->slots);
+                             plan->order, plan->ctl, plan->slot, plan->split_items, max_split, plan->slots);
           m.order = plan->order;
           m.ctl = plan->ctl;
           m.mid = plan->mid;
@@ -1188,15 +1560,16 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
           m.split_items = plan->split_items;
           m.part_o = plan->part_o;
           m.part_lse = plan->part_lse;
-          grid = total + plan->max_split;  // entries: items plus halves of split items
+          grid = total + max_split;  // entries: items plus halves of split items
         }
         hipError_t ev = record_attention_event(0, s);
         if (ev != hipSuccess) return ev;
-        hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
+        if (pair) hipLaunchKernelGGL((bsa_pair_kernel<D, OutT>), dim3(grid), dim3(512), 0, s, m);
+        else hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
         if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
-        if (plan && plan->max_split > 0)
-          hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(plan->max_split, 64)), dim3(256), 0, s,
-                             m);
+        if (max_split > 0)
+          hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(max_split * (pair ? 2 : 1), 64)),
+                             dim3(256), 0, s, m);
       }
       return hipGetLastError();
     }

@@ -95,8 +95,9 @@ struct BsaMulti {
   const int* mid;          // [items] first key block (segment-relative) of a split item's second half
   const int* slot;         // [items] partial slot of a split item
   const int* split_items;  // [max_split] item of each partial slot
-  float* part_o;           // [max_split][2][128][D] normalised partial outputs
-  float* part_lse;         // [max_split][2][128] their LSE (natural log)
+  float* part_o;           // [max_split][2][heads per item][128][D] normalised partial outputs
+  float* part_lse;         // [max_split][2][heads per item][128] their LSE (natural log)
+  int pair;                // 1: an item is a pair of query heads (2p, 2p + 1) of one kv head (pair kernel)
 };
 
 // Device buffers of the work order of a segmented launch.
