@@ -65,12 +65,74 @@ def parse():
     ap.add_argument("--offload", action="store_true",
                     help="history K/V in pinned host cache blocks, kept blocks copied back through a device ring")
     ap.add_argument("--group", type=int, default=8, help="cache blocks per ring group (offload)")
+    ap.add_argument("--default-events", action="store_true",
+                    help="time with torch's default events (system-scope fence at every record) instead of "
+                         "timing-only events")
     ap.add_argument("--no-sub", action="store_true",
                     help="the 32K line without its 128K sub-records (last chunk with cache blocks; 28/4-head layer)")
     ap.add_argument("--fused", action="store_true",
                     help="time each chunk's history + chunk attention as one causal pass (no partials, no merge); "
                          "by default a step is the pages' composition (two segments, LSE merge)")
     return ap.parse_args()
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: recording it performs no system-scope
+    cache writeback / invalidate (the HIP runtime documents the flag for timing events; a default event's fence
+    would cool the caches for the next kernel and stretch the interval).  Interface as torch.cuda.Event's
+    record / elapsed_time; `cuda_event` is the raw handle (the library's measurement hook takes it)."""
+    _hip = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence (timing stays enabled)
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            import re
+            import torch  # noqa: F401  (loads the HIP runtime torch and the library share)
+            maps = open("/proc/self/maps").read()
+            paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", maps)))
+            lib = ctypes.CDLL(paths[0] if paths else "libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self, enable_timing=True):
+        import ctypes
+        h = ctypes.c_void_p()
+        st = self.hip().hipEventCreateWithFlags(ctypes.byref(h), self.FLAGS)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        self.cuda_event = h.value
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "cuda_event", None):
+            self._hip.hipEventDestroy(self.cuda_event)
+            self.cuda_event = None
+
+    def record(self, stream):
+        st = self.hip().hipEventRecord(self.cuda_event, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        st = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+
+def timing_event():
+    import torch
+    return torch.cuda.Event(enable_timing=True) if DEFAULT_EVENTS else TimingEvent()
+
+
+DEFAULT_EVENTS = False
 
 
 def copy_probe(mib):
@@ -177,7 +239,7 @@ def measured_gemm_peak():
     for _ in range(3):
         torch.mm(a, b, out=c)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = timing_event(), timing_event()
     reps = 20
     e0.record(stream)
     for _ in range(reps):
@@ -275,7 +337,7 @@ def measure_varlen(a, w, q, k, v):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     # every event is created before the timed region (creating one can stall the host)
-    ev_pool = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    ev_pool = [[timing_event() for _ in range(6)] for _ in range(a.steps)]
     for e in ev_pool:  # torch creates an event at its first record
         for x in e:
             x.record(stream)
@@ -390,6 +452,8 @@ def main():
     if a.copy_mib:
         copy_probe(a.copy_mib)
         return
+    global DEFAULT_EVENTS
+    DEFAULT_EVENTS = a.default_events
     # no garbage-collector pauses inside the timed regions; collected explicitly between measurements
     gc.disable()
     from block_sparse_attention_xattn_amd import synthetic
@@ -490,10 +554,10 @@ def measure(a, w, q, k, v, fused=None):
     stream = torch.cuda.current_stream()
     ev = []
     # events are created before they are needed (creating one mid-run can stall the host)
-    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(24 * len(run.bufs) * a.steps + 16)]
+    ev_pool = [timing_event() for _ in range(24 * len(run.bufs) * a.steps + 16)]
 
     def mark(tag):
-        e = ev_pool.pop() if ev_pool else torch.cuda.Event(enable_timing=True)
+        e = ev_pool.pop() if ev_pool else timing_event()
         e.record(stream)
         ev.append((tag, e))
 
@@ -534,8 +598,8 @@ def measure(a, w, q, k, v, fused=None):
     B.bsa_prefill_packed, B.bsa_prefill_segments = wrap(orig_bsa), wrap(orig_seg)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0 = timing_event()
+    e1 = timing_event()
     e0.record(stream)
     for _ in range(a.steps):
         run.run()
@@ -597,7 +661,7 @@ def measure(a, w, q, k, v, fused=None):
         oo, lo = torch.empty_like(oa), torch.empty_like(la)
         for _ in range(3):
             B.attn_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)
-        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0, m1 = timing_event(), timing_event()
         m0.record(stream)
         for _ in range(20):
             B.attn_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)
@@ -665,6 +729,11 @@ def measure(a, w, q, k, v, fused=None):
         "estimate_gflop": round(est_flops / 1e9, 1),
         "bsa_gflop": round(bsa_flops_step / 1e9, 1),
         "bsa_useful_tflops": round(split["useful"] * a.steps / (sum(bsa_durs) * 1e-3) / 1e12, 1),
+        # each attention launch of a step (in launch order): its computed-block work and mean event time
+        "bsa_per_launch": [{"gflop": round(f / 1e9, 2),
+                            "ms": round(sum(bsa_durs[i::n_launch]) / a.steps, 4),
+                            "tflops": round(f / (sum(bsa_durs[i::n_launch]) / a.steps * 1e-3) / 1e12, 1)}
+                           for i, f in enumerate(launches)],
         **hbm,
     }
     if a.estimator == "downsampled":

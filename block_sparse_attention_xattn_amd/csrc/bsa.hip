@@ -816,12 +816,21 @@ __global__ __launch_bounds__(512, 1) void bsa3_kernel(BsaMulti M) {
 // stay one phase apart as in the ping-pong form (group 0's matrix phase of
 // block i meets group 1's vector phase of block i-1), and the tiles are double
 // buffered: K of block i in K slot i % 2, V^T of block i in V slot i % 2.
-// Group 1 brings K of block i + 2 during its vector phase of block i (two
-// phases before group 0 needs it; it waits at the end of its next matrix
-// phase), group 0 brings V^T of block i during its vector phase of block i (one
-// phase before its P V^T of block i), so each wave issues eight 1 KiB tile
-// pieces per vector phase instead of sixteen.
+// Group 1 brings K of block i + 2 and V^T of block i + 1 during its vector
+// phase of block i, two phases before group 0 reads them (it waits for them at
+// the end of its next matrix phase); group 0's vector phase is softmax only.
+// A head-block thus costs half the tile loads of the single-head form.
 // ---------------------------------------------------------------------------
+// Pair items take the query heads of kv head v two at a time: (v g, v g + 1), (v g + 2, v g + 3), ...; with an
+// odd group size g the last item of each kv head holds one head (its second group only helps bring the tiles).
+// Item hp (over ceil(g / 2) items per kv head) -> its first query head and its head count.
+__device__ __forceinline__ void pair_heads(int hp, int group, int& h0, int& nh) {
+  const int per = (group + 1) / 2;
+  const int kvh = hp / per, j = hp % per;
+  h0 = kvh * group + 2 * j;
+  nh = 2 * j + 1 < group ? 2 : 1;
+}
+
 template <int D, typename OutT>
 __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams& P, int item, int part, int bid) {
   static_assert(D == 128, "pair form: head_dim 128");
@@ -847,9 +856,11 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
   const int n = lane & 31;
   const int hh = lane >> 5;
 
-  int hp, qb;
-  bsa_decode(bid, P.group / 2, P.hkv, P.n_qb, hp, qb);
-  const int h = 2 * hp + grp;  // this group's query head
+  int hp, qb, h0, nh;
+  bsa_decode(bid, (P.group + 1) / 2, P.hkv, P.n_qb, hp, qb);
+  pair_heads(hp, P.group, h0, nh);
+  const bool active = grp < nh;           // group 1 of a one-head item computes nothing
+  const int h = h0 + (active ? grp : 0);  // this group's query head
   const int kvh = h / P.group;
   const int64_t row0 = (int64_t)qb * kBlk + wave * 32;
   const int64_t wave_q_lo = P.q_start + row0;
@@ -878,13 +889,13 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
   if (part == 1) jb_end = M.mid[item];
   if (part == 2) jb_lo = M.mid[item];
   const uint8_t* mrow0 =
-      P.mask ? P.mask + (int64_t)(2 * hp) * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
-  const uint8_t* mrow1 = P.mask ? mrow0 + P.mask_hs : nullptr;
+      P.mask ? P.mask + (int64_t)h0 * P.mask_hs + (int64_t)qb * P.mask_rs + (gb0 - P.mask_off) : nullptr;
+  const uint8_t* mrow1 = P.mask ? mrow0 + P.mask_hs : nullptr;  // read only when the item has a second head
   const bf16* kg = P.k_hi + (int64_t)kvh * P.k_head;
   const bf16* vg = P.vt_hi + (int64_t)kvh * P.vt_head;
   const int64_t kv_len = P.kv_len, kv_start = P.kv_start, k_tok = P.k_tok, vt_pitch = P.vt_pitch;
   const bool causal = P.causal != 0;
-  const int own_bit = 1 << (kOwnShift + grp);
+  const int own_bit = active ? 1 << (kOwnShift + grp) : 0;
 
   // Piece i of this wave's share of a tile covers rows r = 32 wave + 4 i + lane / 16, lane chunk
   // (lane % 16) ^ (r % 16): byte offset kx[i % 4] + i * 4 rows (as in the ping-pong form).
@@ -935,7 +946,7 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
         const int64_t jb = w0 + 64 * t + lane;
         const bool in = jb < w1;
         const bool a = in && (mrow0 == nullptr || mrow0[jb] != 0);
-        const bool b = in && (mrow1 == nullptr || mrow1[jb] != 0);
+        const bool b = nh == 2 && in && (mrow1 == nullptr || mrow1[jb] != 0);
         tag[t] = (a ? 1 << kOwnShift : 0) | (b ? 2 << kOwnShift : 0);
       }
       const uint64_t bal0 = __ballot(tag[0] != 0);
@@ -954,8 +965,9 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
     __syncthreads();
     const int cnt = s_cnt;
     const int iters = cnt == 0 ? 0 : cnt + 1;
-    // K of the first two blocks: group 0 the first, group 1 the second
+    // K of the first two blocks (group 0 the first, group 1 the second) and V^T of the first (group 1)
     if (grp < cnt) issue_k(entry(grp) & kBlockBits, grp);
+    if (grp == 1 && cnt > 0) issue_v(entry(0) & kBlockBits, 0);
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
     static_assert(NMD == 4, "fragment ring: four output / score tiles");
@@ -992,9 +1004,9 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
           }
       }
     };
-    // vector phase i: group 0 brings V^T of block i, group 1 K of block i + 2; then the softmax of block i
+    // vector phase i: group 1 brings V^T of block i + 1 and K of block i + 2; then the softmax of block i
     auto vphase = [&](int i) {
-      if (grp == 0 && i < cnt) issue_v(entry(i) & kBlockBits, i & 1);
+      if (grp == 1 && i + 1 < cnt) issue_v(entry(i + 1) & kBlockBits, (i + 1) & 1);
       if (grp == 1 && i + 2 < cnt) issue_k(entry(i + 2) & kBlockBits, i & 1);
       if (i < cnt) {
         const int e = entry(i);
@@ -1039,14 +1051,13 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
             }
         }
       }
-      if (grp == 0) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): V^T of block i landed
     };
     // group 1 starts one barrier later (its matrix phase i meets group 0's vector phase i) and group 0 passes
-    // one more barrier at the end; group 1 waits for its K loads at the end of each matrix phase
+    // one more barrier at the end; group 1 waits for its tile loads at the end of each matrix phase
     if (grp == 1) __syncthreads();
     for (int i = 0; i < iters; ++i) {
       mphase(i);
-      if (grp == 1) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): K of block i + 1 landed
+      if (grp == 1) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): K of block i + 1, V^T of block i landed
       __syncthreads();
       vphase(i);
       __syncthreads();
@@ -1062,6 +1073,7 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
     lse_v = (m_run * c + log2f(l_row)) * kLn2;
   }
   if (part != 0) {
+    if (!active) return;
     const size_t ps = ((size_t)(2 * M.slot[item] + part - 1) * 2 + grp) * kBlk + wave * 32 + n;
     float* po = M.part_o + ps * D;
 #pragma unroll
@@ -1075,7 +1087,7 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
     if (hh == 0) M.part_lse[ps] = lse_v;
     return;
   }
-  if (hh == 0) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
+  if (hh == 0 && active) P.lse[(int64_t)h * P.q_len + row0 + n] = lse_v;
   OutT* out = reinterpret_cast<OutT*>(P.out);
   if constexpr (sizeof(OutT) == 2) {
     // both heads' rows through LDS (the tile slots are free: every wave passed the loop's last barrier and
@@ -1101,10 +1113,12 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
     for (int j = 0; j < 8; ++j) {
       const int q = j * 512 + (int)threadIdx.x;
       const int g = q >> 11, r = (q >> 4) & 127, ch = q & 15;
+      if (g >= nh) continue;
       const u32x4 val = *reinterpret_cast<const u32x4*>(smem + (g * 128 + r) * kStgPitch + ch * 16);
-      *reinterpret_cast<u32x4*>(out + (rbase + r) * ((int64_t)P.hq * D) + (int64_t)(2 * hp + g) * D + ch * 8) = val;
+      *reinterpret_cast<u32x4*>(out + (rbase + r) * ((int64_t)P.hq * D) + (int64_t)(h0 + g) * D + ch * 8) = val;
     }
   } else {
+    if (!active) return;
     const int64_t obase = (row0 + n) * ((int64_t)P.hq * D) + (int64_t)h * D;
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
@@ -1243,14 +1257,17 @@ constexpr int kPlanBins = 4096;  // counts >= kPlanBins-1 share the last bin
 constexpr int kMinSplit = 32;    // items with fewer kept tiles are never split
 
 template <int D, typename OutT, bool VARLEN>
-__device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int& h, int& qb, int64_t& jb_end) {
+__device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int& h, int& qb, int64_t& jb_end,
+                                               int& nh) {
   int item0;
   BsaParams P;
   if constexpr (VARLEN) P = varlen_params<D, OutT>(M, item, item0);
   else P = find_seg(M, item, item0);
+  nh = 1;
   if (M.pair) {
-    bsa_decode(item - item0, P.group / 2, P.hkv, P.n_qb, h, qb);
-    h *= 2;  // the pair's first query head
+    int hp;
+    bsa_decode(item - item0, (P.group + 1) / 2, P.hkv, P.n_qb, hp, qb);
+    pair_heads(hp, P.group, h, nh);  // h: the item's first query head
   } else {
     bsa_decode(item - item0, P.group, P.hkv, P.n_qb, h, qb);
   }
@@ -1272,9 +1289,9 @@ __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items
   const int item = (int)blockIdx.x * 4 + wave_id();
   const int lane = lane_id();
   if (item >= n_items) return;
-  int h, qb;
+  int h, qb, nh;
   int64_t jb_end;
-  const BsaParams P = item_span<128, bf16, VARLEN>(M, item, h, qb, jb_end);
+  const BsaParams P = item_span<128, bf16, VARLEN>(M, item, h, qb, jb_end, nh);
   int cnt;
   int64_t half_at;
   if (P.mask == nullptr) {
@@ -1282,7 +1299,7 @@ __global__ __launch_bounds__(256) void plan_count_kernel(BsaMulti M, int n_items
     half_at = jb_end / 2;
   } else {
     const uint8_t* mrow = P.mask + (int64_t)h * P.mask_hs + (int64_t)qb * P.mask_rs + (P.kv_start / kBlk - P.mask_off);
-    const int64_t other = M.pair ? P.mask_hs : 0;  // the pair's second head (itself for single-head items)
+    const int64_t other = nh == 2 ? P.mask_hs : 0;  // the pair's second head (itself for one-head items)
     auto kept_at = [&](int64_t jb) { return (mrow[jb] | mrow[jb + other]) != 0; };
     cnt = 0;
     for (int64_t jb = lane; jb < jb_end; jb += 64) cnt += kept_at(jb);
@@ -1423,10 +1440,11 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
 template <int D, typename OutT, bool VARLEN>
 __device__ void split_merge_one(const BsaMulti& M, int k, int e_head) {
   const int item = M.split_items[k];
-  int h, qb;
+  int h, qb, item_nh;
   int64_t jb_end;
-  const BsaParams P = item_span<D, OutT, VARLEN>(M, item, h, qb, jb_end);
-  const int nh = M.pair ? 2 : 1;  // heads per item; partial (slot k, half p, head e) at ((2 k + p) nh + e) rows
+  const BsaParams P = item_span<D, OutT, VARLEN>(M, item, h, qb, jb_end, item_nh);
+  if (e_head >= item_nh) return;  // the second slot of a one-head pair item
+  const int nh = M.pair ? 2 : 1;  // heads per slot; partial (slot k, half p, head e) at ((2 k + p) nh + e) rows
   h += e_head;
   const float* la = M.part_lse + ((size_t)(2 * k) * nh + e_head) * kBlk;
   const float* lb = la + (size_t)nh * kBlk;
@@ -1464,7 +1482,7 @@ __device__ void split_merge_one(const BsaMulti& M, int k, int e_head) {
   }
 }
 
-// Split halves are merged by a small grid that strides over the slots in use.
+// Split halves are merged by a grid of one workgroup per (slot, head) that may be in use (it strides if smaller).
 template <int D, typename OutT, bool VARLEN>
 __global__ __launch_bounds__(256) void split_merge_kernel(BsaMulti M) {
   const int nh = M.pair ? 2 : 1;
@@ -1531,15 +1549,16 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
     if (tile_offsets_fit(segs, n_seg, D)) {
       BsaMulti m{};
       // pair items (two query heads of one kv head per workgroup) when every segment has an even number of
-      // query heads per kv head and a work order is available; the plan's arrays, sized for single-head
-      // items, hold half as many pair items with two heads per split slot
+      // query heads per kv head and a work order is available (with an odd group size every kv head would
+      // leave a one-head item running at half the rate); the plan's arrays, sized for single-head items, hold
+      // the half as many pair items with two heads per split slot
       bool pair = plan != nullptr && pair_form_enabled();
       for (int i = 0; i < n_seg; ++i) pair = pair && segs[i].group % 2 == 0;
       m.pair = pair ? 1 : 0;
       int total = 0;
       for (int i = 0; i < n_seg; ++i) {
         m.seg[i] = segs[i];
-        total += (pair ? segs[i].hq / 2 : segs[i].hq) * segs[i].n_qb;
+        total += (pair ? segs[i].hkv * ((segs[i].group + 1) / 2) : segs[i].hq) * segs[i].n_qb;
         m.wg_end[i] = total;
       }
       m.n_seg = n_seg;
@@ -1567,9 +1586,10 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
         if (pair) hipLaunchKernelGGL((bsa_pair_kernel<D, OutT>), dim3(grid), dim3(512), 0, s, m);
         else hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
         if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
+        // one workgroup per (split slot, head) that may be in use; the ones past the split count exit
         if (max_split > 0)
-          hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(min(max_split * (pair ? 2 : 1), 64)),
-                             dim3(256), 0, s, m);
+          hipLaunchKernelGGL((split_merge_kernel<D, OutT, false>), dim3(max_split * (pair ? 2 : 1)), dim3(256), 0,
+                             s, m);
       }
       return hipGetLastError();
     }
@@ -1605,7 +1625,7 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   hipLaunchKernelGGL((bsa3_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(512), 0, s, m);
   if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
   if (plan->max_split > 0)
-    hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(min(plan->max_split, 64)), dim3(256), 0, s, m);
+    hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(plan->max_split), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 template hipError_t launch_bsa_varlen<bf16>(const BsaParams&, const VarlenSeq*, int, int, const BsaPlan*,

@@ -445,3 +445,36 @@ def test_rows_longer_than_one_block_list():
         torch.cuda.synchronize()
         ro, rl = O.bsa(_np(q), _np(k), _np(v), kv, 0, mask, 0, False)
         PAR.check_out_lse(_np(out), _np(lse), ro, rl, PAR.OUT_ATOL_BF16)
+
+
+@pytest.mark.parametrize("hq,hkv,density", [(7, 1, 0.5), (6, 2, 0.3), (4, 1, 0.9)])
+def test_segments_head_pairs(hq, hkv, density):
+    """Segmented calls whose items pair up the query heads of a kv head (an odd group size leaves a one-head item
+    per kv head), with per-head random masks (the heads' kept lists differ, so each head must skip the blocks only
+    its partner kept), a history segment long enough to be split and the chunk's own causal segment; out and
+    LSE of every head match the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    d, L, p = 128, 6144, 5632
+    q = _rand((L, hq, d), torch.bfloat16, 95 + hq)
+    k = _rand((L, hkv, d), torch.bfloat16, 96 + hq)
+    v = _rand((L, hkv, d), torch.bfloat16, 97 + hq)
+    qd, kd = q.to(DEV), k.to(DEV)
+    packed = B.PackedV(L, hkv, d, torch.bfloat16, DEV)
+    B.bsa_pack_v(v.to(DEV), packed, 0)
+    rng = np.random.default_rng(hq * 10 + hkv)
+    nqb, nkb = (L - p) // 128, L // 128
+    mask = (rng.random((hq, nqb, nkb)) < density).astype(np.uint8)
+    mask[:, :, 0] = 1
+    md = torch.from_numpy(mask).to(DEV)
+    outs = [(torch.empty(L - p, hq, d, dtype=torch.bfloat16, device=DEV),
+             torch.empty(hq, L - p, dtype=torch.float32, device=DEV)) for _ in range(2)]
+    segs = [dict(k=kd[:p], kv_start=0, v_token_offset=0, block_mask=md, causal=False, out=outs[0][0],
+                 lse=outs[0][1]),
+            dict(k=kd[p:], kv_start=p, v_token_offset=p, block_mask=md, causal=True, out=outs[1][0], lse=outs[1][1])]
+    ws = B.workspace(B.bsa_prefill_segments_workspace_size(L - p, hq, d, 2), DEV)
+    B.bsa_prefill_segments(qd[p:], packed, p, segs, ws=ws)
+    torch.cuda.synchronize()
+    refs = [O.bsa(_np(q[p:]), _np(k[:p]), _np(v[:p]), p, 0, mask, 0, False),
+            O.bsa(_np(q[p:]), _np(k[p:]), _np(v[p:]), p, p, mask, 0, True)]
+    for (go, gl), (ro, rl) in zip(outs, refs):
+        PAR.check_out_lse(_np(go), _np(gl), ro, rl, PAR.OUT_ATOL_BF16)
