@@ -593,6 +593,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
     // contraction step ahead (a ring of four), so an LDS read has four MFMAs to land.
     static_assert(NMD == 4, "fragment ring: four output / score tiles");
     auto mphase = [&](int i) {
+      __builtin_amdgcn_s_setprio(2);  // the matrix phase's MFMAs issue ahead of the other group's softmax
       bf16x8 fr[4];
       if (i >= 1 && i - 1 < n_own) {
 #pragma unroll
@@ -620,6 +621,7 @@ __device__ __forceinline__ void bsa3_body(const BsaMulti& M, const BsaParams& P,
             __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of the next MFMAs
           }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // vector phase i: loads for matrix phase i+1 (K of block i+1, V of block i), softmax of block i
     auto vphase = [&](int i) {
@@ -974,6 +976,9 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
     // matrix phase i: P V^T of block i-1 (V slot (i-1) % 2), then K Q^T of block i (K slot i % 2), each only if
     // this group's head kept the block
     auto mphase = [&](int i) {
+      // Raised issue priority for the matrix phase: the SIMD otherwise favours the older wave, so group 1's MFMAs
+      // waited behind group 0's softmax instructions (its matrix phase ran a quarter longer than group 0's).
+      __builtin_amdgcn_s_setprio(2);
       bf16x8 fr[4];
       if (i >= 1 && (entry(i - 1) & own_bit)) {
         const char* vt = smem + 2 * KTB + ((i - 1) & 1) * VTB;
@@ -1003,6 +1008,7 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
             __builtin_amdgcn_sched_barrier(0);
           }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // vector phase i: group 1 brings V^T of block i + 1 and K of block i + 2; then the softmax of block i
     auto vphase = [&](int i) {
