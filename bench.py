@@ -685,7 +685,11 @@ def measure(a, w, q, k, v, fused=None):
     tokens = len(run.starts) * w["chunk"]
     value = tokens / (step_ms * 1e-3)
     if q.dtype == torch.bfloat16 and w["d"] == 128:
-        kernel_name = "bsa3_kernel<128, bf16> (block-sparse attention)"
+        # the library takes the head-pair form when the query heads per kv head are even (XATTN_PAIR=0 disables it)
+        if (w["hq"] // w["hkv"]) % 2 == 0 and os.environ.get("XATTN_PAIR", "1") != "0":
+            kernel_name = "bsa_pair_kernel<128, bf16> (block-sparse attention, two query heads per workgroup)"
+        else:
+            kernel_name = "bsa3_kernel<128, bf16> (block-sparse attention)"
         timed_call = "the attention kernel alone (events the library records around its launch)"
     else:
         kernel_name = f"bsa_kernel<{w['d']}, {'fp32 as bf16 hi/lo' if q.dtype == torch.float32 else 'bf16'}>"
