@@ -227,7 +227,8 @@ def _attn_mask_strides(m, q, hq, q_len, kv_start, kv_len, mask_kb_offset, block,
 
 def xattn_set_attention_events(before=None, after=None, stream=None):
     """Measurement hook: later attention calls on this thread record the torch.cuda.Event objects
-    `before` / `after` immediately around each launch of the ping-pong attention kernel; (None, None)
+    `before` / `after` immediately around each launch of a ping-pong attention kernel (head-pair or single-head
+    form); (None, None)
     turns it off.  An event torch has not created yet is recorded once on `stream` here so that its
     handle exists."""
     handles = []

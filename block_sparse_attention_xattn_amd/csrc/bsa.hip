@@ -6,16 +6,20 @@
 // .compute_chunked_prefill: the history segment is attended without the
 // causal rule, the chunk's own keys with it, and each part returns (out, lse).
 //
-// Two kernels (gfx950).  bsa3_kernel (bf16, head_dim 128; the hot path) is
-// described above its body below: two groups of four waves alternate matrix
-// and vector phases on alternate kept blocks of one (query head, query block).
+// Three kernels (gfx950), each described above its body below.  bf16,
+// head_dim 128 (the hot path): bsa_pair_kernel (an even number of query heads
+// per kv head) computes two query heads of one kv head per workgroup, its two
+// groups of four waves alternating matrix and vector phases on the union of
+// the two heads' kept blocks; bsa3_kernel (odd group sizes, the packed batch)
+// has both groups on one (query head, query block), on alternate kept blocks.
+// The matrix phases run at raised issue priority.
 // bsa_kernel (XA_F32 inputs, head_dim 64, and tiles whose offsets exceed 32
 // bits):
 //   * one workgroup = one (query head, 128-row query block); 8 waves.  Wave w
 //     owns query rows 32*(w%4) .. +32 and key half 64*(w/4) .. +64 of every
 //     kept key block (split over keys inside the workgroup; the two halves are
 //     merged once at the end through LDS);
-// Both:
+// All:
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     a lane then owns one query row and 16 keys, so the row max / row sum are
 //     mostly in-lane (one cross-half exchange per block for the max);

@@ -61,7 +61,8 @@ const char* xattn_last_error(void);
 const char* xattn_version(void);
 
 /* Measurement hook, not a step of the method.  While set, every call that
- * launches the ping-pong attention kernel (bf16 inputs with head_dim 128
+ * launches a ping-pong attention kernel (the head-pair or the single-head
+ * form; bf16 inputs with head_dim 128
  * through bsa_prefill, bsa_prefill_packed, bsa_prefill_segments,
  * bsa_prefill_varlen or bsa_history_offloaded; fp32 inputs and other head
  * dims run another kernel and record nothing) records `before` on its stream
