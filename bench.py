@@ -232,7 +232,7 @@ def count_flops(run):
 
 def measured_gemm_peak():
     """Dense bf16 GEMM rate of the platform library on this GPU (torch.mm, 8192^3, contiguous operands): the
-    best dense matrix rate measured on the box, reported beside the 2.5 PFLOP/s spec figure."""
+    best dense matrix rate measured on the same GPU, reported beside the 2.5 PFLOP/s spec figure."""
     import torch
     n = 8192
     a = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
