@@ -494,18 +494,25 @@ xa_status_t split_qk(const char* fn, const void* q, int64_t& q_tok, int64_t& q_h
   return XA_OK;
 }
 
-// Attention workgroups resident at once on the current device.
-int resident_workgroups() {
+}  // namespace
+
+namespace xa {
+int device_cus() {
   static int cached[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = bsa_workgroups_per_cu() * cus;
+    cached[dev] = cus;
   }
   return cached[dev];
 }
+}  // namespace xa
+
+namespace {
+// Attention workgroups resident at once on the current device.
+int resident_workgroups() { return bsa_workgroups_per_cu() * device_cus(); }
 
 xa_status_t run_bsa(const char* fn, const BsaParams* segs, int n, int32_t d, xa_dtype_t dtype, xa_dtype_t out_dtype,
                     hipStream_t s, const BsaPlan* plan = nullptr) {

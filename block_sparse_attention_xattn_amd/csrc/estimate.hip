@@ -15,6 +15,10 @@
 //                        query tokens r*S+S-1-t and key tokens c*S+t), then
 //                        per (row, key block) the log-sum-exp of the visible
 //                        scores, written once ([Hq][nKB][R], fp32, log2 units);
+//                        est_gemm2_kernel is the bf16, d = 128 form: 256 x 256
+//                        tiles, one resident workgroup per CU walking every
+//                        grid-th tile, the next tile's first slice loaded
+//                        while the current tile's scores are reduced;
 //   est_select_kernel -- per (head, query block): row normaliser = log-sum-exp
 //                        over key blocks, block score = sum over the block's
 //                        rows of exp2(lse_part - row lse), then the threshold
@@ -192,7 +196,7 @@ __device__ __forceinline__ const VarlenSeq& varlen_seq(const VarlenSeq* seqs, in
 }
 
 template <int HALF>
-__device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
+__device__ __forceinline__ void est_gemm2_body(const EstParams& P, int v0, int vstep, int vend, bool remap) {
   constexpr int TILE = 256;
   constexpr int SLICE_B = TILE * 128;      // one operand slice: 256 rows x 64 bf16
   constexpr int BUF_B = 2 * SLICE_B;       // Q slice + K slice
@@ -207,26 +211,30 @@ __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
 
   const int n_rt = (P.R + TILE - 1) / TILE;
   const int n_ct = (P.N + TILE - 1) / TILE;
-  const int j = w % P.group;
-  w /= P.group;
-  const int rt = w % n_rt;
-  w /= n_rt;
-  const int ct = w % n_ct;
-  const int kvh = w / n_ct;
-  const int h = kvh * P.group + j;
-
   const int64_t cdiag = P.q_start / P.S - P.c0;
-  const int r_hi = min(P.R - 1, rt * TILE + TILE - 1);
-  if ((int64_t)ct * TILE > cdiag + r_hi) return;
 
-  const int w_r0 = rt * TILE + wr * 64;
-  const int w_c0 = ct * TILE + wc * 64;
-  const bool wave_live = w_r0 < P.R && w_c0 < P.N && (int64_t)w_c0 <= cdiag + min(P.R - 1, w_r0 + 63);
+  struct Tile { int rt, ct, h, kvh; };
+  // first tile at or after v with unmasked work (uniform); false when none is left
+  auto next_live = [&](int& v, Tile& t) -> bool {
+    for (; v < vend; v += vstep) {
+      int w = remap ? xcd_remap(v, vend) : v;
+      const int j = w % P.group;
+      w /= P.group;
+      t.rt = w % n_rt;
+      w /= n_rt;
+      t.ct = w % n_ct;
+      t.kvh = w / n_ct;
+      t.h = t.kvh * P.group + j;
+      const int r_hi = min(P.R - 1, t.rt * TILE + TILE - 1);
+      if ((int64_t)t.ct * TILE <= cdiag + r_hi) return true;
+    }
+    return false;
+  };
 
   // this lane's two load chunks per operand per slice (instructions 2*wave, 2*wave+1)
-  const bf16* qb = P.q_hi + (int64_t)h * P.q_head;
-  const bf16* kb = P.k_hi + (int64_t)kvh * P.k_head;
-  auto issue = [&](int slice, int buf) {
+  auto issue = [&](const Tile& T, int slice, int buf) {
+    const bf16* qb = P.q_hi + (int64_t)T.h * P.q_head;
+    const bf16* kb = P.k_hi + (int64_t)T.kvh * P.k_head;
     const int t = slice >> 1;
     const int dof = (slice & 1) * 64;
     char* dq = smem + buf * BUF_B;
@@ -237,9 +245,9 @@ __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
       const int lin = inst * 64 + lane;
       const int r = lin >> 3;
       const int ch = (lin & 7) ^ ((r >> 1) & 7);
-      int qr = rt * TILE + r;
+      int qr = T.rt * TILE + r;
       qr = qr < P.R ? qr : P.R - 1;
-      int kc = ct * TILE + r;
+      int kc = T.ct * TILE + r;
       kc = kc < P.N ? kc : P.N - 1;
       const int64_t qtok = (int64_t)qr * P.S + (P.S - 1 - t);
       const int64_t ktok = (int64_t)kc * P.S + t;
@@ -251,72 +259,91 @@ __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int w) {
     return *reinterpret_cast<const bf16x8*>(base + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
   };
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+  const int n_slices = 2 * P.S;  // even: the last slice reads buffer 1, buffer 0 is free during it
+  int v = v0;
+  Tile cur;
+  if (!next_live(v, cur)) return;
+  issue(cur, 0, 0);
+  while (true) {
+    int vn = v + vstep;
+    Tile nxt;
+    const bool more = next_live(vn, nxt);
 
-  const int n_slices = 2 * P.S;
-  issue(0, 0);
-  for (int sl = 0; sl < n_slices; ++sl) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // this wave's loads of slice sl have landed
-    __syncthreads();                     // ... and every wave's; buffer (sl+1)&1 is free
-    if (sl + 1 < n_slices) issue(sl + 1, (sl + 1) & 1);
+    const int w_r0 = cur.rt * TILE + wr * 64;
+    const int w_c0 = cur.ct * TILE + wc * 64;
+    const bool wave_live = w_r0 < P.R && w_c0 < P.N && (int64_t)w_c0 <= cdiag + min(P.R - 1, w_r0 + 63);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
+
+    for (int sl = 0; sl < n_slices; ++sl) {
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // this wave's loads of slice sl have landed
+      __syncthreads();                     // ... and every wave's; the other buffer is free
+      if (sl + 1 < n_slices) issue(cur, sl + 1, (sl + 1) & 1);
+      else if (more) issue(nxt, 0, 0);
+      if (wave_live) {
+        const char* qs = smem + (sl & 1) * BUF_B;
+        const char* ks = qs + SLICE_B;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8 af[2], bfr[2];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) af[mt] = frag(ks, wc * 64 + mt * 32 + n, 2 * kk + hh);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) bfr[nt] = frag(qs, wr * 64 + nt * 32 + n, 2 * kk + hh);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(af[mt], bfr[nt], acc[mt][nt]);
+        }
+      }
+    }
+
     if (wave_live) {
-      const char* qs = smem + (sl & 1) * BUF_B;
-      const char* ks = qs + SLICE_B;
+      // every column of the wave valid for every row of it: no per-element mask
+      const bool full = w_c0 + 63 < P.N && (int64_t)w_c0 + 63 <= cdiag + w_r0;
+      const float sc = P.scale_log2;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 af[2], bfr[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) af[mt] = frag(ks, wc * 64 + mt * 32 + n, 2 * kk + hh);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) bfr[nt] = frag(qs, wr * 64 + nt * 32 + n, 2 * kk + hh);
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = w_r0 + nt * 32 + n;
+        float x[32];  // raw scores (the scale is positive, so the maximum is taken before scaling)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(af[mt], bfr[nt], acc[mt][nt]);
+          for (int i = 0; i < 16; ++i) x[mt * 16 + i] = acc[mt][nt][i];
+        if (!full) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+              if (!(c < P.N && c <= cdiag + r)) x[mt * 16 + i] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int g0 = 0; g0 < 32; g0 += HALF) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int q = g0; q < g0 + HALF; ++q) mx = fmaxf(mx, x[q]);
+          mx = halves_max(mx);
+          const float ref = mx == -INFINITY ? 0.f : mx * sc;
+          float s = 0.f;
+#pragma unroll
+          for (int q = g0; q < g0 + HALF; ++q) s += fast_exp2(__builtin_fmaf(x[q], sc, -ref));
+          s = halves_sum(s);
+          const int kbk = w_c0 / (2 * HALF) + g0 / HALF;
+          if (hh == 0 && r < P.R && kbk < P.nkb)
+            P.lse_part[((int64_t)cur.h * P.nkb_ld + P.kb0 + kbk) * P.R + r] =
+                mx == -INFINITY ? -INFINITY : ref + log2f(s);
+        }
       }
     }
-  }
-  if (!wave_live) return;
-
-  // every column of the wave valid for every row of it: no per-element mask
-  const bool full = w_c0 + 63 < P.N && (int64_t)w_c0 + 63 <= cdiag + w_r0;
-  const float sc = P.scale_log2;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = w_r0 + nt * 32 + n;
-    float x[32];  // raw scores (the scale is positive, so the maximum is taken before scaling)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[mt * 16 + i] = acc[mt][nt][i];
-    if (!full) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t c = (int64_t)w_c0 + mt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-          if (!(c < P.N && c <= cdiag + r)) x[mt * 16 + i] = -INFINITY;
-        }
-    }
-#pragma unroll
-    for (int g0 = 0; g0 < 32; g0 += HALF) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = g0; v < g0 + HALF; ++v) mx = fmaxf(mx, x[v]);
-      mx = halves_max(mx);
-      const float ref = mx == -INFINITY ? 0.f : mx * sc;
-      float s = 0.f;
-#pragma unroll
-      for (int v = g0; v < g0 + HALF; ++v) s += fast_exp2(__builtin_fmaf(x[v], sc, -ref));
-      s = halves_sum(s);
-      const int kbk = w_c0 / (2 * HALF) + g0 / HALF;
-      if (hh == 0 && r < P.R && kbk < P.nkb)
-        P.lse_part[((int64_t)h * P.nkb_ld + P.kb0 + kbk) * P.R + r] = mx == -INFINITY ? -INFINITY : ref + log2f(s);
-    }
+    if (!more) break;
+    cur = nxt;
+    v = vn;
   }
 }
 
@@ -337,10 +364,10 @@ __global__ __launch_bounds__(1024) void est_gemm2_kernel(EstParams P0) {
     P.nkb = kl / 128;
     P.nkb_ld = P.nkb;
     P.lse_part += rfl64(v.lse_off);
-    est_gemm2_body<HALF>(P, w);
+    est_gemm2_body<HALF>(P, w, 1, w + 1, false);
   } else {
     const int n_rt = (P0.R + 255) / 256, n_ct = (P0.N + 255) / 256;
-    est_gemm2_body<HALF>(P0, xcd_remap(blockIdx.x, P0.hkv * n_ct * n_rt * P0.group));
+    est_gemm2_body<HALF>(P0, blockIdx.x, gridDim.x, P0.hkv * n_ct * n_rt * P0.group, true);
   }
 }
 
@@ -539,7 +566,8 @@ template <int D, bool SPLIT>
 hipError_t launch_est_gemm(const EstParams& p, hipStream_t s) {
   if constexpr (D == 128 && !SPLIT) {
     const int n_rt = (p.R + 255) / 256, n_ct = (p.N + 255) / 256;
-    const int grid = p.hkv * n_ct * n_rt * p.group;
+    // one resident workgroup per CU (128 KiB of LDS each) walks every grid-th tile
+    const int grid = min(p.hkv * n_ct * n_rt * p.group, device_cus());
     switch (p.b) {
       case 8: hipLaunchKernelGGL((est_gemm2_kernel<4, false>), dim3(grid), dim3(1024), 0, s, p); break;
       case 16: hipLaunchKernelGGL((est_gemm2_kernel<8, false>), dim3(grid), dim3(1024), 0, s, p); break;

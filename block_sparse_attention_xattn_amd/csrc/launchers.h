@@ -150,6 +150,8 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
                              const BsaPlan* plan, hipStream_t s);
 // Attention workgroups resident per compute unit (the work order balances over CUs times this).
 int bsa_workgroups_per_cu();
+// Compute units of the current device (cached per device).
+int device_cus();
 // Copy `bytes` (a multiple of 4) of host memory to device memory in stream order through kernel arguments.
 hipError_t upload_words(const void* src, size_t bytes, void* dst, hipStream_t s);
 hipError_t launch_vt(const void* v, xa_dtype_t dt, int64_t v_tok, int64_t v_head, int64_t n_tok, int hkv, int D,
