@@ -38,48 +38,55 @@ __global__ __launch_bounds__(256) void cache_block_kernel(
 }
 
 // Density counts (XAttentionBSAPolicy.select_blocks step 5 and the comm density after its step 6).
-// Workgroups stride over the (head, query block) rows; a row's causal columns are 0 .. diag0 + qb (clipped
-// to the mask); its threads count the kept bytes among them.  Workgroup 0 also counts the kept cache blocks.
-// One 64-bit atomic per counter and workgroup adds the totals to counts[0..3].
-__global__ __launch_bounds__(256) void density_kernel(const uint8_t* __restrict__ mask, int heads, int n_qb,
-                                                      int64_t n_cols, int64_t hs, int64_t rs, int64_t diag0,
-                                                      const uint8_t* __restrict__ keep_any, int64_t n_cb,
-                                                      unsigned long long* counts) {
-  __shared__ unsigned long long s_part[3][4];
+// One wave per (head, query block) row, sixteen rows per workgroup; a row's causal columns are
+// 0 .. diag0 + qb (clipped to the mask) and its lanes count the kept bytes among them.  Workgroup 0 also
+// counts the kept cache blocks.  One 64-bit atomic per counter and workgroup adds the totals to
+// counts[0..3] (few workgroups, so few atomics meet on one address).
+constexpr int kDensityWaves = 16;
+__global__ __launch_bounds__(64 * kDensityWaves) void density_kernel(const uint8_t* __restrict__ mask, int heads,
+                                                                   int n_qb, int64_t n_cols, int64_t hs,
+                                                                   int64_t rs, int64_t diag0,
+                                                                   const uint8_t* __restrict__ keep_any,
+                                                                   int64_t n_cb, unsigned long long* counts) {
+  __shared__ unsigned long long s_part[3][kDensityWaves];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   unsigned long long sel = 0, tot = 0, kept = 0;
   if (mask) {
-    const int rows = heads * n_qb;
-    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
-      const int h = r / n_qb, qb = r % n_qb;
+    const int64_t rows = (int64_t)heads * n_qb;
+    for (int64_t r = (int64_t)blockIdx.x * kDensityWaves + wave; r < rows; r += (int64_t)gridDim.x * kDensityWaves) {
+      const int h = (int)(r / n_qb), qb = (int)(r % n_qb);
       int64_t last = diag0 + qb;
       if (last > n_cols - 1) last = n_cols - 1;
       const uint8_t* row = mask + h * hs + qb * rs;
-      for (int64_t c = threadIdx.x; c <= last; c += blockDim.x) sel += row[c] != 0;
-      if (threadIdx.x == 0 && last >= 0) tot += (unsigned long long)(last + 1);
+#pragma unroll 4
+      for (int64_t c = lane; c <= last; c += 64) sel += row[c] != 0;
+      if (lane == 0 && last >= 0) tot += (unsigned long long)(last + 1);
     }
   }
   if (keep_any && blockIdx.x == 0)
     for (int64_t c = threadIdx.x; c < n_cb; c += blockDim.x) kept += keep_any[c] != 0;
-  // wave sums, then the four waves' partials through LDS
+  // wave sums, then the waves' partials through LDS
   for (int off = 32; off > 0; off >>= 1) {
     sel += __shfl_down(sel, off);
     tot += __shfl_down(tot, off);
     kept += __shfl_down(kept, off);
   }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_part[0][w] = sel;
-    s_part[1][w] = tot;
-    s_part[2][w] = kept;
+  if (lane == 0) {
+    s_part[0][wave] = sel;
+    s_part[1][wave] = tot;
+    s_part[2][wave] = kept;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned long long a = s_part[0][0] + s_part[0][1] + s_part[0][2] + s_part[0][3];
-    const unsigned long long b = s_part[1][0] + s_part[1][1] + s_part[1][2] + s_part[1][3];
+    unsigned long long a = 0, b = 0, c = 0;
+    for (int i = 0; i < kDensityWaves; ++i) {
+      a += s_part[0][i];
+      b += s_part[1][i];
+      c += s_part[2][i];
+    }
     if (a) atomicAdd(&counts[0], a);
     if (b) atomicAdd(&counts[1], b);
     if (blockIdx.x == 0 && keep_any) {
-      const unsigned long long c = s_part[2][0] + s_part[2][1] + s_part[2][2] + s_part[2][3];
       if (c) atomicAdd(&counts[2], c);
       if (n_cb) atomicAdd(&counts[3], (unsigned long long)n_cb);
     }
@@ -135,9 +142,10 @@ extern "C" xa_status_t xattn_density_counts(const uint8_t* block_mask, int32_t h
   if (!block_mask && !keep_any) return XA_OK;
   const int64_t rows = block_mask ? (int64_t)heads * n_qb : 0;
   if (rows > 0x7fffffff) return fail(XA_EUNSUPPORTED, "xattn_density_counts: too many mask rows");
-  const unsigned grid = (unsigned)(rows < 1 ? 1 : (rows < 1024 ? rows : 1024));
+  const int64_t wgs = (rows + kDensityWaves - 1) / kDensityWaves;
+  const unsigned grid = (unsigned)(wgs < 1 ? 1 : (wgs < 128 ? wgs : 128));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(density_kernel, dim3(grid), dim3(256), 0, s, block_mask, block_mask ? heads : 0,
+  hipLaunchKernelGGL(density_kernel, dim3(grid), dim3(64 * kDensityWaves), 0, s, block_mask, block_mask ? heads : 0,
                      block_mask ? n_qb : 1, n_cols, mask_head_stride, mask_row_stride, diag0, keep_any,
                      n_cache_blocks, reinterpret_cast<unsigned long long*>(counts));
   return xa_host::check_launch("xattn_density_counts");

@@ -55,12 +55,15 @@ def test_density_small_chunked_prefill_vs_oracle():
     assert 0.0 < got["density"] <= 1.0
 
 
-@pytest.mark.parametrize("diag0,keep", [(5, True), (0, False), (-3, True), (40, True), (7, None)])
-def test_density_counts_abi_edges(diag0, keep):
-    """Strided mask views, diagonals before / past the mask, no keep list, and accumulation over two calls."""
+@pytest.mark.parametrize("diag0,keep,shape", [(5, True, (3, 6, 13)), (0, False, (3, 6, 13)),
+                                              (-3, True, (3, 6, 13)), (40, True, (3, 6, 13)),
+                                              (7, None, (3, 6, 13)), (250, True, (40, 64, 300))])
+def test_density_counts_abi_edges(diag0, keep, shape):
+    """Strided mask views, diagonals before / past the mask, no keep list, accumulation over two calls, and
+    more rows than the grid holds waves (each wave takes several rows, each lane several columns)."""
     from block_sparse_attention_xattn_amd import binding as B
     rng = np.random.default_rng(diag0 + 10)
-    H, nqb, ncols = 3, 6, 13
+    H, nqb, ncols = shape
     full = (rng.random((H, nqb, ncols + 4)) < 0.5).astype(np.uint8)
     view = torch.from_numpy(full).to(DEV)[:, :, 2:2 + ncols]      # row stride ncols + 4, column offset 2
     m = full[:, :, 2:2 + ncols]
