@@ -195,6 +195,9 @@ __device__ __forceinline__ const VarlenSeq& varlen_seq(const VarlenSeq* seqs, in
   return v;
 }
 
+// The workgroup computes the tiles v = v0, v0 + vstep, ... below vend (mapped through the XCD grouping when
+// remap; the packed batch passes one tile), one after another: the next live tile's first slice is issued into
+// the free buffer at the top of the current tile's last slice, so it lands during that slice and the epilogue.
 template <int HALF>
 __device__ __forceinline__ void est_gemm2_body(const EstParams& P, int v0, int vstep, int vend, bool remap) {
   constexpr int TILE = 256;
