@@ -156,6 +156,26 @@ def test_estimate(case):
     PAR.check_mask(gm.cpu().numpy(), rs, rm, p, tau)
 
 
+def test_estimate_tile_walk_ragged():
+    """More 256 x 256 score tiles than the GPU has compute units, so each workgroup walks several of them and skips
+    the ones right of the causal limit; the last row and column tiles are partial (q_len 4992 at q_start 4096:
+    624 reshaped rows, 1136 reshaped columns at stride 8; 32 query / 8 kv heads, 480 tiles).  Three heads are
+    compared with the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, q_len, p, S, tau = 32, 8, 128, 4992, 4096, 8, 0.9
+    k_len = p + q_len
+    q = _rand((q_len, hq, d), torch.bfloat16, 91)
+    k = _rand((k_len, hkv, d), torch.bfloat16, 92)
+    gs, gm = B.xattn_estimate(q.to(DEV), k.to(DEV), p, S, tau)
+    torch.cuda.synchronize()
+    gs, gm = gs.cpu().numpy(), gm.cpu().numpy()
+    for h in (0, 13, 31):
+        kvh = h // (hq // hkv)
+        rs, rm = O.estimate(_np(q[:, h:h + 1]), _np(k[:, kvh:kvh + 1]), p, S, tau)
+        PAR.check_scores(gs[h:h + 1], rs)
+        PAR.check_mask(gm[h:h + 1], rs, rm, p, tau)
+
+
 # --------------------------------------------------------------------------- composed
 def test_tiny_chunked_prefill_end_to_end():
     """The 1K fp32 workload: 2 query heads sharing 1 kv head, d 64, stride 8, threshold 0.9."""
