@@ -176,6 +176,20 @@ def test_estimate_tile_walk_ragged():
         PAR.check_mask(gm[h:h + 1], rs, rm, p, tau)
 
 
+def test_estimate_long_history_rows():
+    """Rows of 4096 key blocks (q_len 256 at q_start 524032, 2 query heads on one kv head): the selection sorts
+    4096 keys per row (16 per thread) and the GEMM walks 512 tiles; compared whole with the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, q_len, p, S, tau = 2, 1, 128, 256, 524032, 8, 0.9
+    q = _rand((q_len, hq, d), torch.bfloat16, 93)
+    k = _rand((p + q_len, hkv, d), torch.bfloat16, 94)
+    rs, rm = O.estimate(_np(q), _np(k), p, S, tau)
+    gs, gm = B.xattn_estimate(q.to(DEV), k.to(DEV), p, S, tau)
+    torch.cuda.synchronize()
+    PAR.check_scores(gs.cpu().numpy(), rs)
+    PAR.check_mask(gm.cpu().numpy(), rs, rm, p, tau)
+
+
 # --------------------------------------------------------------------------- composed
 def test_tiny_chunked_prefill_end_to_end():
     """The 1K fp32 workload: 2 query heads sharing 1 kv head, d 64, stride 8, threshold 0.9."""
