@@ -190,6 +190,22 @@ def test_estimate_long_history_rows():
     PAR.check_mask(gm.cpu().numpy(), rs, rm, p, tau)
 
 
+def test_estimate_max_key_blocks():
+    """The largest key length the estimate accepts, 8192 key blocks (q_len 128 at q_start 1048448): the selection
+    keeps 8192 sort keys in 64 KiB of dynamic LDS (above the default limit, raised at launch); compared whole with
+    the oracle."""
+    from block_sparse_attention_xattn_amd import binding as B
+    hq, hkv, d, q_len, p, S, tau = 1, 1, 128, 128, 1048448, 8, 0.9
+    q = _rand((q_len, hq, d), torch.bfloat16, 95)
+    k = _rand((p + q_len, hkv, d), torch.bfloat16, 96)
+    rs, rm = O.estimate(_np(q), _np(k), p, S, tau)
+    gs, gm = B.xattn_estimate(q.to(DEV), k.to(DEV), p, S, tau)
+    torch.cuda.synchronize()
+    assert gs.shape[-1] == 8192
+    PAR.check_scores(gs.cpu().numpy(), rs)
+    PAR.check_mask(gm.cpu().numpy(), rs, rm, p, tau)
+
+
 # --------------------------------------------------------------------------- composed
 def test_tiny_chunked_prefill_end_to_end():
     """The 1K fp32 workload: 2 query heads sharing 1 kv head, d 64, stride 8, threshold 0.9."""
