@@ -409,7 +409,10 @@ def measure_varlen(a, w, q, k, v):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "lengths": list(w["lengths"]), "tokens": tokens, "q_heads": run.hq,
                    "kv_heads": run.hkv, "head_dim": run.d, "stride": S, "threshold": tau, "block": 128},
-        "roofline": {"bound": "mfma", "kernel": "bsa3_kernel<128, bf16> packed-batch form (block-sparse attention)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("bsa_pair_kernel<128, bf16> packed-batch form (block-sparse attention, two query heads "
+                                "per workgroup)" if (run.hq // run.hkv) % 2 == 0 and os.environ.get("XATTN_PAIR", "1") != "0"
+                                else "bsa3_kernel<128, bf16> packed-batch form (block-sparse attention)"),
                      "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(achieved / 2500.0, 4), "traffic": None,
                      "avg_launch_ms": round(kern_ms, 4),

@@ -411,16 +411,23 @@ __device__ __forceinline__ const BsaParams& find_seg(const BsaMulti& M, int item
 // Packed batch: the sequence of work item `item` (binary search of the records' item prefix ends,
 // uniform per workgroup) and its problem, seg[0]'s shared fields taken relative to the sequence: its
 // query / key / packed-V rows, causal with the queries at the end of its keys, its compact block mask
-// [hq][q_len/128][k_len/128], its output rows and its LSE block [hq][q_len].
+// [hq][q_len/128][k_len/128], its output rows and its LSE block [hq][q_len].  The records count items
+// per (query head, query block); head-pair items are ceil(group / 2) per kv head and query block.
 template <int D, typename OutT>
 __device__ __forceinline__ BsaParams varlen_params(const BsaMulti& M, int item, int& item0) {
+  const int hq = M.seg[0].hq;
+  const int per_qb = M.pair ? M.seg[0].hkv * ((M.seg[0].group + 1) / 2) : hq;  // items per query block
+  auto end_of = [&](int s) {
+    const int e = __builtin_amdgcn_readfirstlane(M.seqs[s].sel_end);
+    return M.pair ? e / hq * per_qb : e;
+  };
   int lo = 0, hi = M.n_seg - 1;
   while (lo < hi) {
     const int md = (lo + hi) >> 1;
-    if (item < __builtin_amdgcn_readfirstlane(M.seqs[md].sel_end)) hi = md;
+    if (item < end_of(md)) hi = md;
     else lo = md + 1;
   }
-  item0 = lo ? __builtin_amdgcn_readfirstlane(M.seqs[lo - 1].sel_end) : 0;
+  item0 = lo ? end_of(lo - 1) : 0;
   const VarlenSeq& v = M.seqs[lo];
   const int q0 = __builtin_amdgcn_readfirstlane(v.q0);
   const int ql = __builtin_amdgcn_readfirstlane(v.q_len);
@@ -1141,7 +1148,7 @@ __device__ __forceinline__ void bsa_pair_body(const BsaMulti& M, const BsaParams
   }
 }
 
-template <int D, typename OutT>
+template <int D, typename OutT, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bsa_pair_kernel(BsaMulti M) {
   __shared__ int s_item;
   const int n_items = M.n_items;
@@ -1152,8 +1159,13 @@ __global__ __launch_bounds__(512, 1) void bsa_pair_kernel(BsaMulti M) {
   if (e < 0) return;
   const int item = e >> 2, part = e & 3;
   int item0;
-  const BsaParams& P = find_seg(M, item, item0);
-  bsa_pair_body<D, OutT>(M, P, item, part, item - item0);
+  if constexpr (VARLEN) {
+    const BsaParams P = varlen_params<D, OutT>(M, item, item0);
+    bsa_pair_body<D, OutT>(M, P, item, part, item - item0);
+  } else {
+    const BsaParams& P = find_seg(M, item, item0);
+    bsa_pair_body<D, OutT>(M, P, item, part, item - item0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1593,7 +1605,7 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
         }
         hipError_t ev = record_attention_event(0, s);
         if (ev != hipSuccess) return ev;
-        if (pair) hipLaunchKernelGGL((bsa_pair_kernel<D, OutT>), dim3(grid), dim3(512), 0, s, m);
+        if (pair) hipLaunchKernelGGL((bsa_pair_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
         else hipLaunchKernelGGL((bsa3_kernel<D, OutT, false>), dim3(grid), dim3(512), 0, s, m);
         if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
         // one workgroup per (split slot, head) that may be in use; the ones past the split count exit
@@ -1617,12 +1629,19 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   BsaMulti m{};
   m.seg[0] = shared;
   m.n_seg = n_seqs;
-  m.n_items = n_items;
   m.seqs = seqs;
-  hipLaunchKernelGGL(plan_count_kernel<true>, dim3((n_items + 3) / 4), dim3(256), 0, s, m, n_items, plan->weights,
+  // head-pair items for an even number of query heads per kv head, as in the segmented form; n_items counts
+  // (query head, query block) items, and the plan's arrays hold half as many pair items with two heads per
+  // split slot
+  const bool pair = pair_form_enabled() && shared.group % 2 == 0;
+  m.pair = pair ? 1 : 0;
+  const int items = pair ? n_items / 2 : n_items;
+  const int max_split = pair ? plan->max_split / 2 : plan->max_split;
+  m.n_items = items;
+  hipLaunchKernelGGL(plan_count_kernel<true>, dim3((items + 3) / 4), dim3(256), 0, s, m, items, plan->weights,
                      plan->mid);
-  hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, n_items, (const int*)plan->weights, plan->order,
-                     plan->ctl, plan->slot, plan->split_items, plan->max_split, plan->slots);
+  hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(1024), 0, s, items, (const int*)plan->weights, plan->order,
+                     plan->ctl, plan->slot, plan->split_items, max_split, plan->slots);
   m.order = plan->order;
   m.ctl = plan->ctl;
   m.mid = plan->mid;
@@ -1632,10 +1651,11 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   m.part_lse = plan->part_lse;
   hipError_t ev = record_attention_event(0, s);
   if (ev != hipSuccess) return ev;
-  hipLaunchKernelGGL((bsa3_kernel<128, OutT, true>), dim3(n_items + plan->max_split), dim3(512), 0, s, m);
+  if (pair) hipLaunchKernelGGL((bsa_pair_kernel<128, OutT, true>), dim3(items + max_split), dim3(512), 0, s, m);
+  else hipLaunchKernelGGL((bsa3_kernel<128, OutT, true>), dim3(items + max_split), dim3(512), 0, s, m);
   if ((ev = record_attention_event(1, s)) != hipSuccess) return ev;
-  if (plan->max_split > 0)
-    hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(plan->max_split), dim3(256), 0, s, m);
+  if (max_split > 0)
+    hipLaunchKernelGGL((split_merge_kernel<128, OutT, true>), dim3(max_split * (pair ? 2 : 1)), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 template hipError_t launch_bsa_varlen<bf16>(const BsaParams&, const VarlenSeq*, int, int, const BsaPlan*,

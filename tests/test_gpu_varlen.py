@@ -39,10 +39,12 @@ def _batch(lens, seed, hq=4, hkv=2, d=128):
     return q, k, v, cq, ck
 
 
-@pytest.fixture(scope="module")
-def small():
+# 4 query heads on 2 kv heads (attention in head pairs) and 3 on 1 (one query head per workgroup)
+@pytest.fixture(scope="module", params=[(4, 2), (3, 1)], ids=["pairs", "single"])
+def small(request):
     from block_sparse_attention_xattn_amd.varlen import VarlenPrefill
-    q, k, v, cq, ck = _batch(LENS, 30)
+    hq, hkv = request.param
+    q, k, v, cq, ck = _batch(LENS, 30, hq=hq, hkv=hkv)
     run = VarlenPrefill(q.to(DEV), k.to(DEV), v.to(DEV), cq, ck, 8, 0.9)
     run.run()
     torch.cuda.synchronize()
@@ -55,7 +57,7 @@ def test_estimate_varlen_equals_single_and_oracle(small):
     for b, (sc, m) in enumerate(zip(run.block_scores(), run.masks())):
         ql, kl = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
         if ql == 0:
-            assert sc.shape == (4, 0, kl // 128)
+            assert sc.shape == (q.shape[1], 0, kl // 128)
             continue
         p = kl - ql
         rs, rm = B.xattn_estimate(q[cq[b]:cq[b + 1]].to(DEV), k[ck[b]:ck[b + 1]].to(DEV), p, 8, 0.9)
