@@ -10,8 +10,9 @@
 // head_dim 128 (the hot path): bsa_pair_kernel (an even number of query heads
 // per kv head) computes two query heads of one kv head per workgroup, its two
 // groups of four waves alternating matrix and vector phases on the union of
-// the two heads' kept blocks; bsa3_kernel (odd group sizes, the packed batch)
-// has both groups on one (query head, query block), on alternate kept blocks.
+// the two heads' kept blocks (segments, and the packed batch); bsa3_kernel (odd
+// group sizes) has both groups on one (query head, query block), on alternate
+// kept blocks.
 // The matrix phases run at raised issue priority.
 // bsa_kernel (XA_F32 inputs, head_dim 64, and tiles whose offsets exceed 32
 // bits):
