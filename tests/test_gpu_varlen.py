@@ -96,6 +96,34 @@ def test_bsa_varlen_dense_vs_oracle():
         PAR.check_out_lse(_np(run.out[cq[b]:cq[b + 1]]), _np(lses[b]), ro, rl, PAR.OUT_ATOL_BF16)
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (3, 1)], ids=["pairs", "single"])
+@pytest.mark.parametrize("density", [1.0, 0.6])
+def test_bsa_varlen_fp32_out_vs_oracle(hq, hkv, density):
+    """fp32 output of the packed-batch attention (head-pair and single-head forms), dense and with a random block
+    mask per sequence (rows whose mask keeps nothing visible return zeros and an LSE of -inf)."""
+    from block_sparse_attention_xattn_amd import binding as B
+    lens = [(512, 4096), (128, 128), (0, 256), (384, 1280)]
+    q, k, v, cq, ck = _batch(lens, 32, hq=hq, hkv=hkv)
+    qd, kd = q.to(DEV), k.to(DEV)
+    packed = B.PackedV(ck[-1], hkv, 128, torch.bfloat16, DEV)
+    B.bsa_pack_v(v.to(DEV), packed, 0)
+    masks, flat = [], None
+    if density < 1.0:
+        rng = np.random.default_rng(7)
+        masks = [(rng.random((hq, ql // 128, kl // 128)) < density).astype(np.uint8) for ql, kl in lens]
+        flat = torch.from_numpy(np.concatenate([m.ravel() for m in masks])).to(DEV)
+    out = torch.empty(cq[-1], hq, 128, dtype=torch.float32, device=DEV)
+    out, lse = B.bsa_prefill_varlen(qd, kd, packed, cq, ck, flat, out=out)
+    torch.cuda.synchronize()
+    lses = B.varlen_lse(lse, cq, hq)
+    for b, (ql, kl) in enumerate(lens):
+        if ql == 0:
+            continue
+        ro, rl = O.bsa(_np(q[cq[b]:cq[b + 1]]), _np(k[ck[b]:ck[b + 1]]), _np(v[ck[b]:ck[b + 1]]), kl - ql, 0,
+                       masks[b] if masks else None, 0, True)
+        PAR.check_out_lse(_np(out[cq[b]:cq[b + 1]]), _np(lses[b]), ro, rl, PAR.OUT_ATOL_BF16)
+
+
 def test_varlen_workload_full_size():
     from block_sparse_attention_xattn_amd import synthetic
     from block_sparse_attention_xattn_amd.varlen import VarlenPrefill
