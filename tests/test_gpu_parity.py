@@ -497,7 +497,7 @@ def test_rows_longer_than_one_block_list():
         PAR.check_out_lse(_np(out), _np(lse), ro, rl, PAR.OUT_ATOL_BF16)
 
 
-@pytest.mark.parametrize("hq,hkv,density", [(7, 1, 0.5), (6, 2, 0.3), (4, 1, 0.9)])
+@pytest.mark.parametrize("hq,hkv,density", [(7, 1, 0.5), (6, 2, 0.3), (4, 1, 0.9), (16, 2, 0.4)])
 def test_segments_head_pairs(hq, hkv, density):
     """Segmented calls whose items pair up the query heads of a kv head (an odd group size leaves a one-head item
     per kv head), with per-head random masks (the heads' kept lists differ, so each head must skip the blocks only
