@@ -48,7 +48,7 @@ TRAFFIC = {
     ],
     "llama8b_varlen_8seq": [
         {"bsa_code_sha256": "8da9a24475492239a880063536a18d43c6ab6518563421d583f5fe67ef3cee70",
-         "stride": 8, "threshold": 0.9, "fused": False,
+         "stride": 8, "threshold": 0.95, "fused": False,
          "hbm_bytes_per_launch": 6.3684e9},   # fetch 5.9089e9 (x1.9999) + write 4.595e8 (x1.0), head-pair form
     ],
     "gqa7_128k_32x4k": [
