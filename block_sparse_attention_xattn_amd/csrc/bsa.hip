@@ -395,10 +395,19 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-// Next work-order entry for this workgroup, longest first (-1: every entry is taken).
+// Next work-order entry for this workgroup, longest first (-1: every entry is taken).  Workgroups at or past the
+// entry count return before calling this.  The first n = min(M.direct, entries) workgroups (dispatched first, one
+// per resident slot) take the entries 0 .. n-1 without a ticket, each XCD a contiguous run of them (workgroup b
+// runs on XCD b mod 8), so that neighbouring entries (often the query heads of one kv head, reading the same
+// tiles) share an L2; the others take tickets from n on.  A ticket stays below the grid size, which the order
+// array holds, so the entry is read without waiting for the comparison with the entry count.
 __device__ __forceinline__ int take_entry(const BsaMulti& M) {
-  const int t = atomicAdd(&M.ctl[0], 1);
-  return t < M.ctl[1] ? M.order[t] : -1;
+  const int total = M.ctl[1];
+  const int n = M.direct < total ? M.direct : total;
+  const int b = (int)blockIdx.x;
+  const int t = b < n ? xcd_remap(b, n) : n + atomicAdd(&M.ctl[0], 1);
+  const int e = M.order[t];
+  return t < total ? e : -1;
 }
 
 // Segment of work item `item` (kernel-argument segments) and the first item of that segment.
@@ -1602,6 +1611,7 @@ hipError_t launch_bsa(const BsaParams* segs, int n_seg, const BsaPlan* plan, hip
           m.split_items = plan->split_items;
           m.part_o = plan->part_o;
           m.part_lse = plan->part_lse;
+          m.direct = plan->slots;
           grid = total + max_split;  // entries: items plus halves of split items
         }
         hipError_t ev = record_attention_event(0, s);
@@ -1650,6 +1660,7 @@ hipError_t launch_bsa_varlen(const BsaParams& shared, const VarlenSeq* seqs, int
   m.split_items = plan->split_items;
   m.part_o = plan->part_o;
   m.part_lse = plan->part_lse;
+  m.direct = plan->slots;
   hipError_t ev = record_attention_event(0, s);
   if (ev != hipSuccess) return ev;
   if (pair) hipLaunchKernelGGL((bsa_pair_kernel<128, OutT, true>), dim3(items + max_split), dim3(512), 0, s, m);

@@ -98,6 +98,7 @@ struct BsaMulti {
   float* part_o;           // [max_split][2][heads per item][128][D] normalised partial outputs
   float* part_lse;         // [max_split][2][heads per item][128] their LSE (natural log)
   int pair;                // 1: an item is a pair of query heads (2p, 2p + 1) of one kv head (pair kernel)
+  int direct;              // workgroups below this index take order entry blockIdx.x without a ticket
 };
 
 // Device buffers of the work order of a segmented launch.
