@@ -1286,7 +1286,7 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ x,
 // list scheduling), and a last kernel merges the two halves of each split item
 // by their LSE.  The order decides only which workgroup computes what.
 constexpr int kPlanBins = 4096;  // counts >= kPlanBins-1 share the last bin
-constexpr int kMinSplit = 32;    // items with fewer kept tiles are never split
+constexpr int kMinSplit = 20;    // items with fewer kept tiles are never split
 
 template <int D, typename OutT, bool VARLEN>
 __device__ __forceinline__ BsaParams item_span(const BsaMulti& M, int item, int& h, int& qb, int64_t& jb_end,
@@ -1422,7 +1422,7 @@ __global__ __launch_bounds__(1024) void plan_sort_kernel(int n_items, const int*
 #pragma unroll
   for (int w = 0; w < 16; ++w) all += wtot[w];
   const long long thr = all / (slots > 0 ? slots : 1);
-  // halves of fewer than 16 tiles cost more in per-item overhead and merging than they balance
+  // halves of fewer than 10 tiles cost more in per-item overhead and merging than they balance
   auto candidate = [&](int w) { return w >= kMinSplit && (long long)w > thr; };
   for (int i = t; i < n_items; i += 1024) {
     const int w = weights[i];

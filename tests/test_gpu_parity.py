@@ -409,7 +409,7 @@ def test_segments_work_order():
     assert sorted(weights.tolist()) == sorted(expect)
     slots = torch.cuda.get_device_properties(0).multi_processor_count  # one attention workgroup per CU
     thr = int(weights.sum()) // slots
-    split = {i for i in range(n) if weights[i] >= 32 and weights[i] > thr}
+    split = {i for i in range(n) if weights[i] >= 20 and weights[i] > thr}
     # every entry was taken: the first min(slots, grid) workgroups read entries 0 .. slots-1 without a ticket,
     # the others take tickets (counted in ctl[0]) from there on
     assert ctl[1] == n + n_split and n_split == len(split) and slots + ctl[0] >= ctl[1]
