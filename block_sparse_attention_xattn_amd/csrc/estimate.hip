@@ -543,8 +543,10 @@ __device__ __forceinline__ void est_select_body(const SelParams& P, int w) {
 
 template <int B, bool VARLEN>
 __global__ __launch_bounds__(256) void est_select_kernel(SelParams P0) {
+  // each XCD a contiguous range of (head, query block): neighbouring query blocks read the two halves of the
+  // same 128-byte lines of the per-block log-sum-exp rows
+  int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   if constexpr (VARLEN) {
-    int w = (int)blockIdx.x;
     int q0, ql, k0, kl;
     const VarlenSeq& v = varlen_seq<true>(P0.seqs, P0.n_seqs, w, q0, ql, k0, kl);
     SelParams P = P0;
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(256) void est_select_kernel(SelParams P0) {
     P.npow_cap = np;
     est_select_body<B>(P, w);
   } else {
-    est_select_body<B>(P0, (int)blockIdx.x);
+    est_select_body<B>(P0, w);
   }
 }
 
