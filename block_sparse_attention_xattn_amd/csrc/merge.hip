@@ -20,7 +20,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* __restrict__ o_a, c
                                                     int heads, int head_dim, int lanes) {
   const int64_t rows = q_len * heads;
   const int rows_per_block = blockDim.x / lanes;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / lanes;
+  // each XCD a contiguous range of rows, so the neighbouring tokens' LSE reads share cache lines in its L2
+  const int64_t blk = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int64_t row = blk * rows_per_block + threadIdx.x / lanes;
   const int sub = threadIdx.x % lanes;
   if (row >= rows) return;
   const int64_t tok = row / heads;
