@@ -8,24 +8,31 @@
 
 namespace xa {
 
-// One workgroup per cache block.  Threads stride over the (head, query block)
-// rows; each reads its row's sub_blocks mask bytes, writes the per-head byte
-// and votes into the union.
+// One workgroup per cache block, each XCD a contiguous range of them (neighbouring cache blocks read and
+// write bytes of the same cache lines).  Threads stride over the (head, query block) rows; each reads its
+// row's sub_blocks mask bytes (one 8-byte load where they are 8 and aligned), writes the per-head byte and
+// votes into the union.
 __global__ __launch_bounds__(256) void cache_block_kernel(
     const uint8_t* __restrict__ mask, int heads, int n_qb, int64_t n_cols, int64_t hs, int64_t rs,
     int64_t kb_begin, int64_t n_cb, int sub, int force_first_last, uint8_t* keep_per_head,
     uint8_t* keep_any, uint8_t* keep_any_blocks) {
-  const int64_t cb = blockIdx.x;
+  const int64_t cb = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int64_t c0 = kb_begin + cb * sub;
   int64_t c1 = c0 + sub;
   if (c1 > n_cols) c1 = n_cols;
+  const bool vec8 = c1 - c0 == 8 && ((reinterpret_cast<uintptr_t>(mask) | (uint64_t)hs | (uint64_t)rs |
+                                      (uint64_t)c0) & 7) == 0;
   const int rows = heads * n_qb;
   int any = 0;
   for (int r = threadIdx.x; r < rows; r += blockDim.x) {
     const int h = r / n_qb, qb = r % n_qb;
     const uint8_t* row = mask + h * hs + qb * rs;
     int hit = 0;
-    for (int64_t c = c0; c < c1; ++c) hit |= row[c];
+    if (vec8) {
+      hit = *reinterpret_cast<const uint64_t*>(row + c0) != 0;
+    } else {
+      for (int64_t c = c0; c < c1; ++c) hit |= row[c];
+    }
     hit = hit ? 1 : 0;
     if (keep_per_head) keep_per_head[((int64_t)h * n_qb + qb) * n_cb + cb] = (uint8_t)hit;
     any |= hit;
