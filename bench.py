@@ -39,22 +39,22 @@ TRAFFIC = {
     "llama8b_32k_8x4k": [
         {"bsa_code_sha256": "6d816bdc561e74ce02b5ef8660bd3174e7864ee27c5de32b2b2fdd7953965947",
          "stride": 8, "threshold": 0.95, "fused": False,
-         "hbm_bytes_per_launch": 1.0143e9},   # fetch 9.419e8 (x1.9999) + write 7.24e7 (x1.0), mean of 8 chunks
+         "hbm_bytes_per_launch": 1.0083e9},   # fetch 9.359e8 (x1.9999) + write 7.24e7 (x1.0), mean of 8 chunks
     ],
     "llama8b_128k_last_chunk": [
         {"bsa_code_sha256": "6d816bdc561e74ce02b5ef8660bd3174e7864ee27c5de32b2b2fdd7953965947",
          "stride": 8, "threshold": 0.9, "fused": False,
-         "hbm_bytes_per_launch": 9.1006e9},   # fetch 9.0241e9 (x1.9999) + write 7.66e7 (x1.0)
+         "hbm_bytes_per_launch": 8.9808e9},   # fetch 8.9043e9 (x1.9999) + write 7.66e7 (x1.0)
     ],
     "llama8b_varlen_8seq": [
         {"bsa_code_sha256": "6d816bdc561e74ce02b5ef8660bd3174e7864ee27c5de32b2b2fdd7953965947",
          "stride": 8, "threshold": 0.95, "fused": False,
-         "hbm_bytes_per_launch": 6.1293e9},   # fetch 5.6698e9 (x1.9999) + write 4.595e8 (x1.0), head-pair form
+         "hbm_bytes_per_launch": 6.3071e9},   # fetch 5.8476e9 (x1.9999) + write 4.595e8 (x1.0), head-pair form
     ],
     "gqa7_128k_32x4k": [
         {"bsa_code_sha256": "6d816bdc561e74ce02b5ef8660bd3174e7864ee27c5de32b2b2fdd7953965947",
          "stride": 8, "threshold": 0.9, "fused": False,
-         "hbm_bytes_per_launch": 3.2839e9},   # fetch 3.2251e9 (x1.9999) + write 5.88e7 (x1.0), mean of 32 chunks
+         "hbm_bytes_per_launch": 3.3164e9},   # fetch 3.2576e9 (x1.9999) + write 5.88e7 (x1.0), mean of 32 chunks
     ],
 }
 
